@@ -1,0 +1,36 @@
+"""CPU oracle for the FlashAttention forward pass.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The library under
+``flashattention_forward_amd`` never imports, links or runs anything here,
+and this package imports nothing from it: the two share no code.
+
+Everything is plain numpy in fp64 (exact integer arithmetic for the
+quantised scores), evaluated the obvious way so a reader can check it
+against the sources by eye.
+
+Sources, cited by short name in the modules:
+  [trading post]  "Can a full trading day of context beat one minute? Flash
+                  attention and the sequence-length question" (marketmaker.cc
+                  blog, Thai edition) -- sections "Why attention is bound to
+                  memory", "The Flash Attention algorithm", "The online softmax
+                  recurrence", "Backward: recompute instead of store",
+                  "FA2", "Causal masking", "Integration in eight lines",
+                  "Validation".
+  [FA4 post]      "FlashAttention 4: fast, memory-efficient attention for LLMs"
+                  (linux-konsole.com, Vietnamese) -- "Introduction", "Why
+                  attention kernels still dominate".
+  [INT-FA post]   "INT-FlashAttention: an INT8 quantisation architecture
+                  compatible with FlashAttention" (hoodcat.net, Spanish).
+
+Modules:
+  attention   -- the plain definition (two-pass softmax, fp64).
+  recurrence  -- the tiled online-softmax recurrence exactly as the trading
+                 post's algorithm section states it, plus the merge of
+                 partial states over disjoint key ranges.
+  quant       -- int8 per-token and OCP e4m3 quantisation emulation and the
+                 quantised-attention oracle.
+
+Parity status of every function is stated in its module header.
+"""
+from . import attention, quant, recurrence  # noqa: F401

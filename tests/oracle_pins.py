@@ -1,0 +1,307 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Every pin takes the function under test as an argument, so the same checks
+run against the oracle (tests/test_oracle_pins.py) and against deliberately
+broken copies of it (tests/test_oracle_mutations.py), which must fail at
+least one pin each.
+
+``attn(q, k, v, scale, causal) -> (O, LSE)`` works on one head, fp64.
+Each pin raises AssertionError on failure.
+"""
+from __future__ import annotations
+
+import math
+
+import mpmath
+import numpy as np
+import torch
+
+_RNG = np.random.default_rng(20261203)
+
+
+def _rand(*shape, scale=1.0):
+    return _RNG.standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- attention
+
+def pin_bruteforce(attn, tol=1e-13):
+    """40-digit scalar loops on tiny inputs.  The softmax is evaluated as
+    exp(s - LSE) with LSE = log(sum exp(s)) -- no max subtraction, a different
+    evaluation path from the oracle's."""
+    mpmath.mp.dps = 40
+    for (Nq, Nk, d, dv, causal) in [(1, 1, 1, 1, False), (3, 5, 2, 3, False),
+                                    (4, 4, 4, 2, True), (2, 6, 3, 4, True),
+                                    (6, 6, 1, 1, True), (5, 8, 4, 4, False)]:
+        q, k, v = _rand(Nq, d), _rand(Nk, d), _rand(Nk, dv)
+        scale = 1.0 / math.sqrt(d) if d > 1 else 0.7
+        O, L = attn(q, k, v, scale, causal)
+        for i in range(Nq):
+            vis = [j for j in range(Nk) if (not causal) or j <= i + Nk - Nq]
+            s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[i, t]) * mpmath.mpf(k[j, t]) for t in range(d))
+                 for j in vis]
+            lse = mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))
+            assert abs(float(lse) - L[i]) <= tol * max(1.0, abs(float(lse))), (i, float(lse), L[i])
+            for c in range(dv):
+                oc = mpmath.fsum(mpmath.exp(x - lse) * mpmath.mpf(v[j, c]) for x, j in zip(s, vis))
+                assert abs(float(oc) - O[i, c]) <= tol, (i, c, float(oc), O[i, c])
+
+
+def pin_torch(attn, tol=1e-12):
+    """torch's CPU float64 attention routines (library): O from
+    scaled_dot_product_attention (bottom-right causal via causal_lower_right
+    when Nq < Nk), LSE from the CPU flash-attention op (natural log)."""
+    from torch.nn.attention.bias import causal_lower_right
+    for (Nq, Nk, d, causal) in [(7, 7, 8, False), (7, 7, 8, True), (5, 13, 4, False),
+                                (5, 13, 4, True), (33, 33, 16, True), (1, 9, 8, True)]:
+        q, k, v = _rand(Nq, d), _rand(Nk, d), _rand(Nk, d)
+        scale = 1.0 / math.sqrt(d)
+        O, L = attn(q, k, v, scale, causal)
+        tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+        if causal and Nq != Nk:
+            to = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, attn_mask=causal_lower_right(Nq, Nk), scale=scale)
+        else:
+            to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+        assert np.max(np.abs(to[0, 0].numpy() - O)) <= tol
+        if (not causal) or Nq == Nk:
+            _, tl = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(
+                tq, tk, tv, 0.0, causal, scale=scale)
+            assert np.max(np.abs(tl[0, 0].numpy() - L)) <= tol
+
+
+def pin_uniform(attn, tol=1e-13):
+    """Q = 0: every visible score is 0, so O is the mean of the visible V
+    rows and LSE = ln(#visible keys) (closed form)."""
+    for (Nq, Nk, d, causal) in [(4, 9, 3, False), (6, 6, 5, True), (3, 8, 2, True)]:
+        q = np.zeros((Nq, d))
+        k, v = _rand(Nk, d), _rand(Nk, 4)
+        O, L = attn(q, k, v, 0.3, causal)
+        for i in range(Nq):
+            n = (i + Nk - Nq + 1) if causal else Nk
+            assert np.max(np.abs(O[i] - v[:n].mean(axis=0))) <= tol
+            assert abs(L[i] - math.log(n)) <= tol
+
+
+def pin_onehot(attn, tol=1e-12):
+    """One dominant score per row (margin 60): O_i = V_{t(i)} and
+    LSE_i = s_{i,t(i)} up to e^-60 (closed form)."""
+    Nk, d = 6, 8
+    k = np.zeros((Nk, d))
+    k[np.arange(Nk), np.arange(Nk)] = 1.0          # orthonormal keys
+    t = np.array([4, 0, 5, 2, 2])
+    q = 60.0 * k[t] + 0.0
+    v = _rand(Nk, 3)
+    O, L = attn(q, k, v, 1.0, False)
+    assert np.max(np.abs(O - v[t])) <= tol
+    assert np.max(np.abs(L - 60.0)) <= tol
+
+
+def pin_permutation(attn, tol=1e-12):
+    """Non-causal attention is invariant under one permutation applied to
+    the rows of K and V together."""
+    q, k, v = _rand(5, 4), _rand(11, 4), _rand(11, 6)
+    p = _RNG.permutation(11)
+    O1, L1 = attn(q, k, v, 0.5, False)
+    O2, L2 = attn(q, k[p], v[p], 0.5, False)
+    assert np.max(np.abs(O1 - O2)) <= tol and np.max(np.abs(L1 - L2)) <= tol
+
+
+def pin_key_shift(attn, tol=1e-12):
+    """K <- K + 1 u^T adds scale * q_i.u to every score of row i: O is
+    unchanged and LSE_i moves by scale * q_i.u (integer data, exact)."""
+    q = _RNG.integers(-3, 4, (5, 4)).astype(float)
+    k = _RNG.integers(-3, 4, (9, 4)).astype(float)
+    v = _rand(9, 2)
+    u = np.array([1.0, -2.0, 0.0, 3.0])
+    O1, L1 = attn(q, k, v, 0.25, False)
+    O2, L2 = attn(q, k + u[None, :], v, 0.25, False)
+    assert np.max(np.abs(O1 - O2)) <= tol
+    assert np.max(np.abs((L2 - L1) - 0.25 * (q @ u))) <= tol
+
+
+def pin_causal_prefix(attn, tol=1e-12):
+    """Causal row i equals non-causal attention over keys 0..i+Nk-Nq; row 0
+    of a square problem is V_0 with LSE = s_00."""
+    for (Nq, Nk) in [(7, 7), (4, 10)]:
+        q, k, v = _rand(Nq, 3), _rand(Nk, 3), _rand(Nk, 2)
+        O, L = attn(q, k, v, 0.6, True)
+        for i in range(Nq):
+            n = i + Nk - Nq + 1
+            Oi, Li = attn(q[i:i + 1], k[:n], v[:n], 0.6, False)
+            assert np.max(np.abs(O[i] - Oi[0])) <= tol and abs(L[i] - Li[0]) <= tol
+        if Nq == Nk:
+            assert np.max(np.abs(O[0] - v[0])) <= tol
+            assert abs(L[0] - 0.6 * float(q[0] @ k[0])) <= tol
+
+
+def pin_scale(attn, tol=1e-12):
+    """attn(Q, K, V, c) == attn(c Q, K, V, 1): the scale multiplies scores."""
+    q, k, v = _rand(4, 5), _rand(7, 5), _rand(7, 3)
+    O1, L1 = attn(q, k, v, 0.37, False)
+    O2, L2 = attn(0.37 * q, k, v, 1.0, False)
+    assert np.max(np.abs(O1 - O2)) <= tol and np.max(np.abs(L1 - L2)) <= tol
+
+
+ATTENTION_PINS = [pin_bruteforce, pin_torch, pin_uniform, pin_onehot, pin_permutation,
+                  pin_key_shift, pin_causal_prefix, pin_scale]
+
+
+def pin_rows_sum_to_one(softmax_rows, tol=1e-13):
+    """Rows of P are non-negative and sum to 1, P = 0 exactly where masked."""
+    s = _rand(6, 9) * 3
+    s[2, 5:] = -np.inf
+    P, m, l = softmax_rows(s)
+    assert np.all(P >= 0)
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= tol
+    assert np.all(P[2, 5:] == 0)
+    assert np.allclose(m, s.max(axis=1))
+
+
+# ---------------------------------------------------------------- recurrence
+
+def pin_recurrence_equals_definition(tiled, definition, tol=1e-12):
+    """The tiled recurrence equals the two-pass definition (the trading post's
+    online-softmax section states they agree in exact arithmetic)."""
+    for (Nq, Nk, d, causal, br, bc) in [(9, 13, 4, False, 4, 3), (16, 16, 8, True, 5, 7),
+                                        (5, 12, 3, True, 2, 1), (20, 20, 4, True, 16, 16),
+                                        (7, 30, 6, False, 7, 64), (12, 12, 2, True, 3, 4)]:
+        q, k, v = _rand(Nq, d) * 2, _rand(Nk, d) * 2, _rand(Nk, 5)
+        O1, L1 = tiled(q, k, v, 0.4, causal, B_r=br, B_c=bc)
+        O2, L2 = definition(q, k, v, 0.4, causal)
+        assert np.max(np.abs(O1 - O2)) <= tol and np.max(np.abs(L1 - L2)) <= tol
+
+
+def pin_merge(merge, definition, tol=1e-12):
+    """Merging partial states over a partition of the keys gives the
+    whole-range result; an empty part (LSE = -inf) has no weight."""
+    q, k, v = _rand(6, 4), _rand(23, 4), _rand(23, 3)
+    O, L = definition(q, k, v, 0.5, False)
+    for bounds in ([0, 23], [0, 10, 23], [0, 1, 2, 7, 15, 23]):
+        Os, Ls = [], []
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            o, l = definition(q, k[a:b], v[a:b], 0.5, False)
+            Os.append(o)
+            Ls.append(l)
+        Os.append(np.zeros_like(Os[0]))
+        Ls.append(np.full_like(Ls[0], -np.inf))
+        Om, Lm = merge(np.stack(Os), np.stack(Ls))
+        assert np.max(np.abs(Om - O)) <= tol and np.max(np.abs(Lm - L)) <= tol
+
+
+# ---------------------------------------------------------------- quantisation
+
+def pin_e4m3_decode(decode):
+    """All 256 codes decode like torch's float8_e4m3fn (library); NaN codes
+    are exactly 0x7F and 0xFF."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = decode(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+    assert float(np.nanmax(got)) == 448.0 and decode(np.array([1], np.uint8))[0] == 2.0 ** -9
+
+
+def _e4m3_sweep():
+    """fp32 values around every representable magnitude and every midpoint."""
+    mags = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mids = (mags[:-1] + mags[1:]) / 2
+    pts = np.concatenate([mags, mids]).astype(np.float32)
+    nxt = np.nextafter(pts, np.float32(np.inf))
+    prv = np.nextafter(pts, np.float32(-np.inf))
+    rnd = (_RNG.random(20000) * 460).astype(np.float32)
+    tiny = (_RNG.random(5000) * 2.0 ** -5).astype(np.float32)
+    x = np.concatenate([pts, nxt, prv, rnd, tiny])
+    x = x[(x >= 0) & (x < 464)]
+    return np.concatenate([x, -x]).astype(np.float32)
+
+
+def pin_e4m3_encode(encode, decode):
+    """Round-to-nearest-even encoding: equals torch's fp32 -> float8_e4m3fn
+    cast below the NaN threshold 464, round-trips every finite code, and
+    saturates to +-448 from 448 up (reading: saturating cast)."""
+    x = _e4m3_sweep()
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = encode(x)
+    bad = np.nonzero(ref != got)[0]
+    assert bad.size == 0, (x[bad[:5]], ref[bad[:5]], got[bad[:5]])
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(encode(decode(finite)), finite)
+    big = np.array([448.0, 463.9, 464.0, 1000.0, 1e30], np.float32)
+    assert np.all(encode(big) == 0x7E) and np.all(encode(-big) == 0xFE)
+
+
+def pin_int8_per_token(quantize):
+    """Per-token int8 equals torch: s = amax/127 (fp32), q = torch.round(x/s)
+    (half to even), clamped to +-127; a zero row gives s = 0, q = 0."""
+    x = (_RNG.standard_normal((40, 64)) * _RNG.random((40, 1)) * 5).astype(np.float32)
+    x[3] = 0.0
+    x[5, :4] = [127.0, -63.5, 0.5, -2.5]
+    x[5, 4:] = 0.0
+    # a row where x * (1/s) and x / s round to different integers (-57 vs -58)
+    x[6] = 0.0
+    x[6, :2] = np.array([0x4020B342, 0xBF918415], np.uint32).view(np.float32)
+    q8, s = quantize(x)
+    tx = torch.from_numpy(x)
+    ts = tx.abs().amax(dim=-1) / 127.0
+    tq = torch.where(ts[:, None] > 0, torch.round(tx / torch.where(ts > 0, ts, 1.0)[:, None]),
+                     torch.zeros_like(tx)).clamp(-127, 127).to(torch.int8)
+    assert np.array_equal(s, ts.numpy())
+    assert np.array_equal(q8, tq.numpy())
+    assert list(q8[5, :4]) == [127, -64, 0, -2] and s[3] == 0 and not q8[3].any()
+    assert list(q8[6, :2]) == [127, -58]
+
+
+def pin_qk_int(qk):
+    """Integer scores equal Python-int brute force (exact)."""
+    a = _RNG.integers(-127, 128, (5, 32)).astype(np.int8)
+    b = _RNG.integers(-127, 128, (7, 32)).astype(np.int8)
+    a[0] = 127
+    b[0] = -127
+    got = qk(a, b)
+    for i in range(5):
+        for j in range(7):
+            assert int(got[i, j]) == sum(int(a[i, t]) * int(b[j, t]) for t in range(32))
+    assert int(got[0, 0]) == -127 * 127 * 32
+
+
+def pin_q8_attention(attn_q8, decode, tol=1e-13):
+    """Closed forms under quantisation: (a) Q8 = 0 gives P = 1 = E4M3(1) for
+    every key, so O = mean of the decoded V times s_v and LSE = ln Nk;
+    (b) one key dominant by far more than 2^-10 resolution: O = its decoded
+    V row times s_v; (c) two keys with P = (1, 0.3): E4M3(0.3) = 0.3125 enters
+    P.V while l = 1.3 keeps the unquantised sum."""
+    Nk, d = 10, 16
+    v8 = _RNG.integers(0, 256, (Nk, 8)).astype(np.uint8)
+    v8[(v8 & 0x7F) == 0x7F] = 0x11
+    sv = np.float32(0.125)
+    vdec = decode(v8) * float(sv)
+    k8 = _RNG.integers(-127, 128, (Nk, d)).astype(np.int8)
+    sk = np.full(Nk, 0.01, np.float32)
+    O, L = attn_q8(np.zeros((3, d), np.int8), np.full(3, 0.02, np.float32), k8, sk, v8, sv, 0.25)
+    assert np.max(np.abs(O - vdec.mean(axis=0))) <= tol and np.max(np.abs(L - math.log(Nk))) <= tol
+    k8 = np.zeros((Nk, d), np.int8)
+    k8[np.arange(Nk), np.arange(Nk)] = 127
+    q8 = np.zeros((2, d), np.int8)
+    q8[0, 7] = 127
+    q8[1, 2] = 127
+    O, L = attn_q8(q8, np.full(2, 0.05, np.float32), k8, np.full(Nk, 0.05, np.float32), v8, sv, 1.0)
+    assert np.max(np.abs(O - vdec[[7, 2]])) <= tol
+    assert np.max(np.abs(L - float(np.float32(0.05)) ** 2 * 127 * 127)) <= 1e-12
+    # (c): s_1 - s_0 = ln 0.3 via the k scales
+    k8 = np.zeros((2, d), np.int8)
+    k8[:, 0] = 1
+    q8 = np.zeros((1, d), np.int8)
+    q8[0, 0] = 1
+    sk = np.array([1.0, 1.0], np.float32)
+    sq = np.array([1.0], np.float32)
+    v8b = np.array([[0x38] * 8, [0x40] * 8], np.uint8)       # rows 1.0 and 2.0
+    O, L = attn_q8(q8, sq, k8, sk, v8b, np.float32(1.0), 1.0)
+    assert abs(O[0, 0] - 1.5) <= tol and abs(L[0] - (1.0 + math.log(2.0))) <= tol   # equal scores: P = (1, 1)
+    sk = np.array([1.0, np.float32(1.0 + math.log(0.3))], np.float32)
+    O, L = attn_q8(q8, sq, k8, sk, v8b, np.float32(1.0), 1.0)
+    p1 = math.exp(float(sk[1]) - 1.0)
+    assert abs(O[0, 0] - (1.0 + 0.3125 * 2.0) / (1.0 + p1)) <= 1e-12
+    assert abs(L[0] - (1.0 + math.log1p(p1))) <= 1e-12
