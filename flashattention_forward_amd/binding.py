@@ -1,0 +1,219 @@
+"""Thin ctypes binding of libattn_mi355x.so.
+
+Argument marshalling only: torch allocates device memory and supplies the
+current HIP stream; every step of the attention computation runs in the
+library's kernels.  If the library is missing the import fails loudly --
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_mi355x.so")
+
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1, -2, -3, -4
+ATTN_BF16, ATTN_FP16 = 0, 1
+
+# Every symbol include/attn_mi355x.h declares, with its ctypes signature.
+_P, _I, _L, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "attn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_fwd_decode_splits": (_I, [_I, _I, _I, _I]),
+    "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "attn_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_quantize_rows_i8": (_I, [_P, _P, _P, _L, _I, _P]),
+    "attn_quantize_e4m3_workspace_bytes": (_Z, [_L]),
+    "attn_quantize_tensor_e4m3": (_I, [_P, _P, _P, _L, _P, _Z, _P]),
+    "attn_fwd_q8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_debug_qk_i32": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "attn_debug_cvt_e4m3": (_I, [_P, _P, _L, _P]),
+    "attn_status_str": (ctypes.c_char_p, [_I]),
+    "attn_build_info": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m flashattention_forward_amd.build` "
+                               "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(rc: int) -> str:
+    return lib().attn_status_str(rc).decode()
+
+
+def build_info() -> str:
+    return lib().attn_build_info().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != ATTN_OK:
+        raise RuntimeError(f"{what}: {status_str(rc)} (code {rc})")
+
+
+# --------------------------------------------------------------- torch side
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_FP16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def workspace_bytes(B, H, Nq, Nk, d, dtype_code) -> int:
+    return int(lib().attn_fwd_workspace_bytes(B, H, Nq, Nk, d, dtype_code))
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+             workspace=None, want_lse: bool = True):
+    """O, LSE = attention(q, k, v) for [B, H, N, d] bf16/fp16 GPU tensors."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
+        raise ValueError("q, k, v must be [B, H, N, d] with matching B, H, d and K/V lengths")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    wsb = workspace_bytes(B, H, Nq, Nk, d, code)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
+    rc = lib().attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                        _dev(lse, "lse") if lse is not None else None, B, H, Nq, Nk, d, scale,
+                        int(bool(causal)), code,
+                        _dev(workspace, "workspace") if workspace is not None else None,
+                        workspace.numel() if workspace is not None else 0, _stream())
+    _check(rc, "attn_fwd")
+    return out, lse
+
+
+def decode_splits(B, H, Nk, d) -> int:
+    return int(lib().attn_fwd_decode_splits(B, H, Nk, d))
+
+
+def attn_fwd_decode(q, k, v, num_splits: int, scale: float | None = None, out=None, lse=None, workspace=None):
+    """Split-KV decode: q [B, H, 1, d] against k, v [B, H, Nk, d]."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if Nq != 1:
+        raise ValueError("decode takes one query per (batch, head)")
+    code = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, 1), device=q.device, dtype=torch.float32) if lse is None else lse
+    wsb = int(lib().attn_decode_workspace_bytes(B, H, d, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), device=q.device, dtype=torch.uint8)
+    rc = lib().attn_fwd_decode(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
+                               B, H, Nk, d, scale, code, num_splits, _dev(workspace, "workspace"),
+                               workspace.numel(), _stream())
+    _check(rc, "attn_fwd_decode")
+    return out, lse
+
+
+def quantize_rows_i8(x):
+    """Per-token int8 of a bf16 [..., d] tensor -> (int8 [..., d], fp32 scales [...])."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16:
+        raise ValueError("quantize_rows_i8 takes bf16")
+    d = x.shape[-1]
+    rows = x.numel() // d
+    x8 = torch.empty(x.shape, device=x.device, dtype=torch.int8)
+    s = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32)
+    _check(lib().attn_quantize_rows_i8(_dev(x, "x"), _dev(x8, "x8"), _dev(s, "scales"), rows, d, _stream()),
+           "attn_quantize_rows_i8")
+    return x8, s
+
+
+def quantize_tensor_e4m3(x, workspace=None):
+    """Per-tensor E4M3 of a bf16 tensor -> (uint8 codes, fp32 scale as a 1-element GPU tensor)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16:
+        raise ValueError("quantize_tensor_e4m3 takes bf16")
+    n = x.numel()
+    x8 = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
+    s = torch.empty(1, device=x.device, dtype=torch.float32)
+    wsb = int(lib().attn_quantize_e4m3_workspace_bytes(n))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), device=x.device, dtype=torch.uint8)
+    _check(lib().attn_quantize_tensor_e4m3(_dev(x, "x"), _dev(x8, "x8"), _dev(s, "scale"), n,
+                                           _dev(workspace, "workspace"), workspace.numel(), _stream()),
+           "attn_quantize_tensor_e4m3")
+    return x8, s
+
+
+def attn_fwd_q8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
+                out=None, lse=None):
+    """Quantised forward: int8 q8/k8 [B,H,N,d] with per-token scales, E4M3 v8 with a
+    per-tensor scale (1-element GPU tensor).  Returns (O bf16, LSE fp32)."""
+    torch = _torch()
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
+    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
+    rc = lib().attn_fwd_q8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
+                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
+                           B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
+    _check(rc, "attn_fwd_q8")
+    return out, lse
+
+
+def debug_qk_i32(q8, k8):
+    """int32 Q8 K8^T of one head through the quantised kernel's tile routine."""
+    torch = _torch()
+    Nq, d = q8.shape
+    Nk = k8.shape[0]
+    s = torch.empty((Nq, Nk), device=q8.device, dtype=torch.int32)
+    _check(lib().attn_debug_qk_i32(_dev(q8, "q8"), _dev(k8, "k8"), _dev(s, "s"), Nq, Nk, d, _stream()),
+           "attn_debug_qk_i32")
+    return s
+
+
+def debug_cvt_e4m3(x):
+    """E4M3 codes of an fp32 GPU tensor through the library's conversion routine."""
+    torch = _torch()
+    y = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
+    _check(lib().attn_debug_cvt_e4m3(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream()), "attn_debug_cvt_e4m3")
+    return y

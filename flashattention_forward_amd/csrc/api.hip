@@ -1,0 +1,154 @@
+// C ABI of libattn_mi355x.so: argument validation and kernel dispatch.
+// Every check runs on the host before anything is launched; an error return
+// means no work was enqueued.  See include/attn_mi355x.h for the contract.
+#include <cmath>
+#include <climits>
+#include <cstdint>
+
+#include "attn_mi355x.h"
+#include "internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+// grid of the prefill kernels: ceil(Nq / 128) * B * H workgroups, must fit an int
+bool prefill_grid_ok(int B, int H, int Nq) {
+  const long long g = ((long long)Nq + 127) / 128 * (long long)B * (long long)H;
+  return g <= INT_MAX;
+}
+
+int check_common(const void* q, const void* k, const void* v, const void* out, const float* lse, int B, int H, int Nq,
+                 int Nk, float scale, int causal) {
+  if (!q || !k || !v || !out) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_INVALID;
+  if (lse && !aligned4(lse)) return ATTN_E_INVALID;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_E_INVALID;
+  if (!good_scale(scale)) return ATTN_E_INVALID;
+  if (causal && Nq > Nk) return ATTN_E_INVALID;
+  if (!prefill_grid_ok(B, H, Nq)) return ATTN_E_INVALID;
+  return ATTN_OK;
+}
+
+bool decode_sizes_ok(int B, int H, int splits) { return (long long)B * H * splits <= INT_MAX; }
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 1 || H < 1 || (d != 64 && d != 128) || num_splits < 1 || num_splits > 256) return 0;
+  return attn::decode_workspace_bytes(B, H, d, num_splits);
+}
+
+int attn_fwd_decode_splits(int B, int H, int Nk, int d) {
+  if (B < 1 || H < 1 || Nk < 1) return 0;
+  return attn::decode_default_splits(B, H, Nk, d);
+}
+
+size_t attn_fwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128) || (dtype != ATTN_BF16 && dtype != ATTN_FP16))
+    return 0;
+  if (Nq != 1) return 0;
+  return attn::decode_workspace_bytes(B, H, d, attn::decode_default_splits(B, H, Nk, d));
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nk, int d,
+                    float scale, int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(q, k, v, out, lse, B, H, 1, Nk, scale, 0);
+  if (rc != ATTN_OK) return rc;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (num_splits < 1 || num_splits > 256 || num_splits > Nk) return ATTN_E_INVALID;
+  if (!decode_sizes_ok(B, H, num_splits)) return ATTN_E_INVALID;
+  const size_t need = attn::decode_workspace_bytes(B, H, d, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ATTN_E_WORKSPACE;
+  return hip_status(attn::launch_decode(q, k, v, out, lse, B, H, Nk, d, scale, dtype == ATTN_BF16, num_splits,
+                                        workspace, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq, int Nk, int d,
+             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(q, k, v, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (Nq == 1) {
+    const int splits = attn::decode_default_splits(B, H, Nk, d);
+    return attn_fwd_decode(q, k, v, out, lse, B, H, Nk, d, scale, dtype, splits, workspace, workspace_bytes, stream);
+  }
+  return hip_status(attn::launch_prefill(q, k, v, out, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype == ATTN_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int attn_quantize_rows_i8(const void* x, int8_t* x8, float* scales, long rows, int d, void* stream) {
+  if (!x || !x8 || !scales || rows < 1) return ATTN_E_INVALID;
+  if (!aligned16(x) || !aligned16(x8) || !aligned4(scales)) return ATTN_E_INVALID;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if ((rows + 15) / 16 > INT_MAX) return ATTN_E_INVALID;
+  return hip_status(attn::launch_quantize_rows_i8(x, x8, scales, rows, d, static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_quantize_e4m3_workspace_bytes(long n) {
+  if (n < 8 || n % 8) return 0;
+  return attn::quantize_e4m3_workspace_bytes(n);
+}
+
+int attn_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_out, long n, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!x || !x8 || !scale_out || n < 8 || n % 8) return ATTN_E_INVALID;
+  if (!aligned16(x) || !aligned16(x8) || !aligned4(scale_out)) return ATTN_E_INVALID;
+  if (!workspace || workspace_bytes < attn::quantize_e4m3_workspace_bytes(n) || !aligned4(workspace))
+    return ATTN_E_WORKSPACE;
+  return hip_status(
+      attn::launch_quantize_tensor_e4m3(x, x8, scale_out, n, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8, const float* q_scale, const float* k_scale,
+                const float* v_scale, void* out, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                int causal, void* stream) {
+  int rc = check_common(q8, k8, v8, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (!q_scale || !k_scale || !v_scale || !aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale))
+    return ATTN_E_INVALID;
+  if (d != 128) return ATTN_E_UNSUPPORTED;
+  return hip_status(attn::launch_prefill_q8(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, B, H, Nq, Nk, d, scale,
+                                            causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+int attn_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d, void* stream) {
+  if (!q8 || !k8 || !s || Nq < 1 || Nk < 1) return ATTN_E_INVALID;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned4(s)) return ATTN_E_INVALID;
+  if (d != 128) return ATTN_E_UNSUPPORTED;
+  return hip_status(attn::launch_debug_qk_i32(q8, k8, s, Nq, Nk, d, static_cast<hipStream_t>(stream)));
+}
+
+int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream) {
+  if (!x || !y || n < 2 || n % 2) return ATTN_E_INVALID;
+  if (!aligned4(x)) return ATTN_E_INVALID;
+  if ((n / 2 + 255) / 256 > INT_MAX) return ATTN_E_INVALID;
+  return hip_status(attn::launch_debug_cvt_e4m3(x, y, n, static_cast<hipStream_t>(stream)));
+}
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_INVALID: return "invalid argument (null/misaligned pointer, bad size or scale, causal with Nq > Nk)";
+    case ATTN_E_UNSUPPORTED: return "unsupported head size or dtype";
+    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_build_info(void) {
+  return "libattn_mi355x: gfx950; prefill bf16/fp16 d={64,128} BM=128 BN=64 4 waves (32 rows/wave), "
+         "32x32x16 MFMA, S^T=KQ^T, V^T via ds_read_b64_tr_b16, rescale threshold 2^8; "
+         "decode split-KV 256 threads, 8 rows in flight/lane + LSE merge; "
+         "q8 prefill d=128 int8 32x32x32 + fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8";
+}
+
+}  // extern "C"

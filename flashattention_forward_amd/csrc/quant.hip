@@ -1,0 +1,477 @@
+// Quantised attention forward for gfx950: int8 scores, fp8 (OCP E4M3) P.V.
+//
+// Follows the token-level INT8 scheme of the hoodcat.net post
+// "INT-FlashAttention: an INT8 quantisation architecture compatible with
+// FlashAttention" (integer GEMM for Q K^T with one fp32 scale per token of Q
+// and of K), with V in E4M3 under one per-tensor scale and P cast to E4M3
+// before the P.V product.  The tiled online softmax is the same as in the
+// 16-bit prefill kernel (see prefill.hip); what changes:
+//   * S^T = K8 Q8^T on v_mfma_i32_32x32x32_i8 with exact int32 accumulation
+//     (|S| <= 127^2 d < 2^24, so the conversion to fp32 is exact too);
+//     scores are acc * k_scale[key] * (q_scale[q] * scale * log2 e);
+//   * P^T is converted to E4M3 in registers (v_cvt_pk_fp8_f32, round to
+//     nearest even) and fed to v_mfma_f32_32x32x64_f8f6f4 as the B operand:
+//     a lane's 32 values of a 64-key tile are exactly one k-step;
+//   * the V8 tile is written to LDS with its rows permuted so that the 32
+//     keys each half-wave holds in the S^T accumulator are 32 consecutive
+//     LDS rows; four transposing 8-bit LDS reads (ds_read_b64_tr_b8) then
+//     give every lane its 32 V values in the same key order;
+//   * l sums the fp32 P (only the MFMA operand is quantised) and the epilogue
+//     applies v_scale / l.
+// The quantisation kernels (per-token int8, per-tensor E4M3) and two test
+// hooks that run this file's own tile routines live here as well.
+#include "common.h"
+#include "internal.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kRescaleThresholdQ = 8.0f;
+
+template <int CTRL>
+__device__ __forceinline__ float dppq(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// max over aligned groups of G lanes (8 or 16), every lane gets it
+template <int G>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dppq<0xB1>(x));
+  x = fmaxf(x, dppq<0x4E>(x));
+  if (G == 16) {
+    x = fmaxf(x, dppq<0x124>(x));
+    x = fmaxf(x, dppq<0x128>(x));
+  } else {
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x101F)));
+  }
+  return x;
+}
+
+__device__ __forceinline__ float block_max_256(float x, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// E4M3 (OCP FN) codes of four floats, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3x4_sat(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+// Same without the clamp, for values known to be within [0, 448] (P).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(u32x4 u, float* f) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __builtin_bit_cast(float, u[j] << 16);
+    f[2 * j + 1] = __builtin_bit_cast(float, u[j] & 0xFFFF0000u);
+  }
+}
+
+// ------------------------------------------------------------ per-token int8
+template <int D>
+__global__ __launch_bounds__(256) void quantize_rows_i8_kernel(const uint16_t* __restrict__ X, int8_t* __restrict__ X8,
+                                                               float* __restrict__ S, long rows) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int ch = threadIdx.x % LPR;
+  const bool valid = row < rows;
+  float f[8];
+  u32x4 u = {0u, 0u, 0u, 0u};
+  if (valid) u = reinterpret_cast<const u32x4*>(X + row * D)[ch];
+  bf16x8_to_f32(u, f);
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+  amax = group_max<LPR>(amax);
+  const float s = amax / 127.0f;  // IEEE division
+  uint32_t lo = 0, hi = 0;
+  if (s > 0.f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float q = fminf(fmaxf(__builtin_rintf(f[j] / s), -127.f), 127.f);
+      const uint32_t b = (uint32_t)((int)q) & 0xFFu;
+      if (j < 4) lo |= b << (8 * j);
+      else hi |= b << (8 * (j - 4));
+    }
+  }
+  if (valid) {
+    u32x2 o;
+    o[0] = lo;
+    o[1] = hi;
+    reinterpret_cast<u32x2*>(X8 + row * D)[ch] = o;
+    if (ch == 0) S[row] = s;
+  }
+}
+
+// ------------------------------------------------------------ per-tensor E4M3
+constexpr int kMaxPartials = 1024;
+
+int e4m3_grid(long n) {
+  const long chunks = n / 8;
+  long g = (chunks + 255) / 256;
+  if (g > kMaxPartials) g = kMaxPartials;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+__global__ __launch_bounds__(256) void amax_partial_kernel(const uint16_t* __restrict__ X, long chunks,
+                                                           float* __restrict__ partial) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (long)gridDim.x * 256) {
+    float f[8];
+    bf16x8_to_f32(reinterpret_cast<const u32x4*>(X)[c], f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+  }
+  m = block_max_256(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(const uint16_t* __restrict__ X, long chunks,
+                                                            const float* __restrict__ partial, int npart,
+                                                            uint8_t* __restrict__ X8, float* __restrict__ scale_out) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < npart; i += 256) m = fmaxf(m, partial[i]);
+  m = block_max_256(m, red);
+  const float s = m / 448.0f;  // IEEE division
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (long)gridDim.x * 256) {
+    u32x2 o = {0u, 0u};
+    if (s > 0.f) {
+      float f[8];
+      bf16x8_to_f32(reinterpret_cast<const u32x4*>(X)[c], f);
+      o[0] = e4m3x4_sat(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
+      o[1] = e4m3x4_sat(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
+    }
+    reinterpret_cast<u32x2*>(X8)[c] = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void debug_cvt_e4m3_kernel(const float* __restrict__ x, uint8_t* __restrict__ y, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (2 * i + 1 < n) {
+    const uint32_t r = e4m3x4_sat(x[2 * i], x[2 * i + 1], 0.f, 0.f);
+    y[2 * i] = r & 0xFFu;
+    y[2 * i + 1] = (r >> 8) & 0xFFu;
+  }
+}
+
+// ------------------------------------------------------------ quantised tiles
+struct Q8Cfg {
+  static constexpr int D = 128, BM = 128, BN = 64, NT = 256;
+  static constexpr int KSTRIDE = D + 16;   // LDS bytes per K8 row
+  static constexpr int VSTRIDE = D + 32;   // LDS bytes per (permuted) V8 row
+  static constexpr int KBYTES = BN * KSTRIDE;
+  static constexpr int VBYTES = BN * VSTRIDE;
+  static constexpr int CPR = D / 16;       // 16-byte chunks per row
+  static constexpr int RPP = NT / CPR;     // rows per staging pass (32)
+  static constexpr int PASSES = BN / RPP;  // 2
+  static constexpr int KSTEPS = D / 32;    // int8 MFMA k-steps
+  static constexpr int MB_O = D / 32;
+};
+
+// Row of the V8 tile in LDS for tile key kt = 8a + 4h + b: 32h + 4a + b.
+__device__ __forceinline__ int v8_lds_row(int kt) { return ((kt >> 2) & 1) * 32 + (kt >> 3) * 4 + (kt & 3); }
+
+// B operand of S^T = K8 Q8^T: lane holds Q8[qrow][32kk + 16h .. +15].
+__device__ __forceinline__ void load_q8_operand(const int8_t* Q8row, bool valid, int h, i32x4* qop) {
+#pragma unroll
+  for (int kk = 0; kk < Q8Cfg::KSTEPS; ++kk) {
+    i32x4 x = {0, 0, 0, 0};
+    if (valid) x = reinterpret_cast<const i32x4*>(Q8row)[2 * kk + h];
+    qop[kk] = x;
+  }
+}
+
+// Exact int32 S^T for the 64 keys of the K8 tile in LDS and the lane's query:
+// acc[nb][i] = sum_t K8[32nb + 8(i/4) + 4h + i%4][t] * Q8[q][t].
+__device__ __forceinline__ void qk_tile_i8(const char* lk, const i32x4* qop, int l32, int h, i32x16* acc) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    acc[nb] = i32x16{};
+#pragma unroll
+    for (int kk = 0; kk < Q8Cfg::KSTEPS; ++kk) {
+      const i32x4 a = lds_load<i32x4>(lk, (32 * nb + l32) * Q8Cfg::KSTRIDE + 32 * kk + 16 * h);
+      acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[kk], acc[nb], 0, 0, 0);
+    }
+  }
+}
+
+// Stage rows [kv0, kv0 + 64) of K8 (and optionally V8) into registers; rows
+// at or beyond Nk read as zero.
+struct Q8Stage {
+  u32x4 k[Q8Cfg::PASSES], v[Q8Cfg::PASSES];
+  float ks;
+  __device__ __forceinline__ void load(const int8_t* K8, const uint8_t* V8, const float* KS, int kv0, int Nk, int tid,
+                                       bool with_v) {
+#pragma unroll
+    for (int p = 0; p < Q8Cfg::PASSES; ++p) {
+      const int row = p * Q8Cfg::RPP + tid / Q8Cfg::CPR, ch = tid % Q8Cfg::CPR;
+      const int key = kv0 + row;
+      k[p] = u32x4{0u, 0u, 0u, 0u};
+      v[p] = u32x4{0u, 0u, 0u, 0u};
+      if (key < Nk) {
+        k[p] = reinterpret_cast<const u32x4*>(K8 + (size_t)key * Q8Cfg::D)[ch];
+        if (with_v) v[p] = reinterpret_cast<const u32x4*>(V8 + (size_t)key * Q8Cfg::D)[ch];
+      }
+    }
+    ks = 0.f;
+    if (KS != nullptr && tid < Q8Cfg::BN && kv0 + tid < Nk) ks = KS[kv0 + tid];
+  }
+  __device__ __forceinline__ void store(char* lk, char* lv, float* lks, int tid, bool with_v) const {
+#pragma unroll
+    for (int p = 0; p < Q8Cfg::PASSES; ++p) {
+      const int row = p * Q8Cfg::RPP + tid / Q8Cfg::CPR, ch = tid % Q8Cfg::CPR;
+      lds_store<u32x4>(lk, row * Q8Cfg::KSTRIDE + ch * 16, k[p]);
+      if (with_v) lds_store<u32x4>(lv, v8_lds_row(row) * Q8Cfg::VSTRIDE + ch * 16, v[p]);
+    }
+    if (lks != nullptr && tid < Q8Cfg::BN) lks[tid] = ks;
+  }
+};
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
+    const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
+    const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, float c, int nqb, int total) {
+  using C = Q8Cfg;
+  __shared__ __attribute__((aligned(16))) char smem[C::KBYTES + C::VBYTES];
+  __shared__ __attribute__((aligned(16))) float lks[C::BN];
+  char* lk = smem;
+  char* lv = smem + C::KBYTES;
+
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int bh = logical / nqb;
+  int qb = logical - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int q0 = qb * C::BM;
+  const int off = Nk - Nq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t qbase = (size_t)bh * Nq, kbase = (size_t)bh * Nk;
+  const int8_t* Kh = K8 + kbase * C::D;
+  const uint8_t* Vh = V8 + kbase * C::D;
+  const float* KSh = KS + kbase;
+
+  const int qrow = q0 + 32 * w + l32;
+  i32x4 qop[C::KSTEPS];
+  load_q8_operand(Q8 + (qbase + qrow) * C::D, qrow < Nq, h, qop);
+  const float cq = (qrow < Nq ? QS[qbase + qrow] : 0.f) * c;
+
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
+  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+
+  f32x16 o[C::MB_O];
+#pragma unroll
+  for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int qmin_w = q0 + 32 * w;
+
+  Q8Stage st;
+  st.load(Kh, Vh, KSh, 0, Nk, tid, true);
+  st.store(lk, lv, lks, tid, true);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) st.load(Kh, Vh, KSh, (t + 1) * C::BN, Nk, tid, true);
+    const int kv0 = t * C::BN;
+    const bool skip = CAUSAL && (kv0 > qmin_w + 31 + off);
+    if (!skip) {
+      i32x16 acc[2];
+      qk_tile_i8(lk, qop, l32, h, acc);
+      f32x16 s[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 ks4 = lds_load<f32x4>(reinterpret_cast<const char*>(lks), (32 * nb + 8 * g + 4 * h) * 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[nb][4 * g + j] = (float)acc[nb][4 * g + j] * ks4[j] * cq;
+        }
+      const bool need_mask = (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
+      if (need_mask) {
+        const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
+          }
+      }
+      float mt = s[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+      mt = fmaxf(mt, swap_halves(mt));
+      if (__any(mt > m_run + kRescaleThresholdQ)) {
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+#pragma unroll
+        for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+        l_run *= alpha;
+        m_run = mn;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      // P^T as 32 E4M3 bytes: byte j <-> s[j / 16][j % 16]
+      i32x8 pb;
+#pragma unroll
+      for (int jw = 0; jw < 8; ++jw) {
+        const int nb = jw >> 2, i0 = 4 * (jw & 3);
+        const float p0 = __builtin_amdgcn_exp2f(s[nb][i0 + 0] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(s[nb][i0 + 1] - m_use);
+        const float p2 = __builtin_amdgcn_exp2f(s[nb][i0 + 2] - m_use);
+        const float p3 = __builtin_amdgcn_exp2f(s[nb][i0 + 3] - m_use);
+        l_run += (p0 + p1) + (p2 + p3);
+        pb[jw] = (int)e4m3x4(p0, p1, p2, p3);
+      }
+      // O^T += V^T P^T: lane (h, d) reads LDS rows 32h .. 32h+31 at column d
+      const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+      for (int mb = 0; mb < C::MB_O; ++mb) {
+        i32x8 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t addr = (32 * h + 8 * r + (r16 >> 1)) * C::VSTRIDE + 32 * mb + 16 * g1 + 8 * (r16 & 1);
+          const i32x2 x = lds_read_tr8(lv, addr);
+          a[2 * r] = x[0];
+          a[2 * r + 1] = x[1];
+        }
+        o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 0, 0, 127, 0, 127);
+      }
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      st.store(lk, lv, lks, tid, true);
+      __syncthreads();
+    }
+  }
+
+  const float l_tot = l_run + swap_halves(l_run);
+  const float f = *VS / l_tot;
+  if (qrow < Nq) {
+    uint16_t* dst = O + (qbase + qrow) * C::D;
+#pragma unroll
+    for (int mb = 0; mb < C::MB_O; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x2 x0 = Mfma<true>::pack2(o[mb][4 * g + 0] * f, o[mb][4 * g + 1] * f);
+        const bf16x2 x1 = Mfma<true>::pack2(o[mb][4 * g + 2] * f, o[mb][4 * g + 3] * f);
+        u32x2 u;
+        u[0] = __builtin_bit_cast(uint32_t, x0);
+        u[1] = __builtin_bit_cast(uint32_t, x1);
+        *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g + 4 * h) = u;
+      }
+    if (LSE != nullptr && h == 0) LSE[qbase + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// Test hook: the exact int32 scores of one head through qk_tile_i8.
+__global__ __launch_bounds__(256) void debug_qk_i32_kernel(const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8,
+                                                           int32_t* __restrict__ S, int Nq, int Nk) {
+  using C = Q8Cfg;
+  __shared__ __attribute__((aligned(16))) char lk[C::KBYTES];
+  const int q0 = blockIdx.x * C::BM, kv0 = blockIdx.y * C::BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int qrow = q0 + 32 * w + l32;
+  i32x4 qop[C::KSTEPS];
+  load_q8_operand(Q8 + (size_t)qrow * C::D, qrow < Nq, h, qop);
+  Q8Stage st;
+  st.load(K8, nullptr, nullptr, kv0, Nk, tid, false);
+  st.store(lk, nullptr, nullptr, tid, false);
+  __syncthreads();
+  i32x16 acc[2];
+  qk_tile_i8(lk, qop, l32, h, acc);
+  if (qrow < Nq) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (key < Nk) S[(size_t)qrow * Nk + key] = acc[nb][i];
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows_i8(const void* x, int8_t* x8, float* scales, long rows, int d, hipStream_t stream) {
+  if (d == 128) {
+    const long grid = (rows + 15) / 16;
+    hipLaunchKernelGGL(quantize_rows_i8_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), x8, scales, rows);
+  } else if (d == 64) {
+    const long grid = (rows + 31) / 32;
+    hipLaunchKernelGGL(quantize_rows_i8_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), x8, scales, rows);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+size_t quantize_e4m3_workspace_bytes(long n) { return (size_t)e4m3_grid(n) * sizeof(float); }
+
+hipError_t launch_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_out, long n, void* workspace,
+                                       hipStream_t stream) {
+  const long chunks = n / 8;
+  const int g = e4m3_grid(n);
+  float* partial = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(256), 0, stream, static_cast<const uint16_t*>(x), chunks,
+                     partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quantize_e4m3_kernel, dim3(g), dim3(256), 0, stream, static_cast<const uint16_t*>(x), chunks,
+                     partial, g, x8, scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8, const float* q_scale,
+                             const float* k_scale, const float* v_scale, void* out, float* lse, int B, int H, int Nq,
+                             int Nk, int d, float scale, bool causal, hipStream_t stream) {
+  if (d != Q8Cfg::D) return hipErrorInvalidValue;
+  const int nqb = (Nq + Q8Cfg::BM - 1) / Q8Cfg::BM;
+  const int total = nqb * B * H;
+  if (causal)
+    hipLaunchKernelGGL(prefill_q8_kernel<true>, dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8, q_scale, k_scale,
+                       v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb, total);
+  else
+    hipLaunchKernelGGL(prefill_q8_kernel<false>, dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8, q_scale, k_scale,
+                       v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d,
+                               hipStream_t stream) {
+  if (d != Q8Cfg::D) return hipErrorInvalidValue;
+  dim3 grid((Nq + Q8Cfg::BM - 1) / Q8Cfg::BM, (Nk + Q8Cfg::BN - 1) / Q8Cfg::BN);
+  hipLaunchKernelGGL(debug_qk_i32_kernel, grid, dim3(256), 0, stream, q8, k8, s, Nq, Nk);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_cvt_e4m3(const float* x, uint8_t* y, long n, hipStream_t stream) {
+  const long pairs = n / 2;
+  hipLaunchKernelGGL(debug_cvt_e4m3_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, stream, x, y, n);
+  return hipGetLastError();
+}
+
+}  // namespace attn

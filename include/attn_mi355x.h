@@ -1,0 +1,167 @@
+/*
+ * attn_mi355x.h -- C ABI of the MI355X (gfx950) FlashAttention forward library
+ * (libattn_mi355x.so).
+ *
+ * What the library computes.  For every batch b and head h, exact attention
+ *     O = softmax(Q K^T * scale) V
+ * ("Why attention is bound to memory" in the marketmaker.cc post "Can a full
+ * trading day of context beat one minute? Flash attention and the
+ * sequence-length question"; "Introduction" of the linux-konsole.com post
+ * "FlashAttention 4: fast, memory-efficient attention for LLMs"), computed
+ * tile by tile with the online-softmax recurrence of that post's sections
+ * "The Flash Attention algorithm" and "The online softmax recurrence", so the
+ * Nq x Nk score matrix never reaches device memory.  Next to O the library
+ * writes the per-row log-sum-exp
+ *     LSE[b,h,i] = ln sum_{j visible} exp(scale * q_i . k_j)
+ * (natural log; the stored softmax statistics (m, l) of "Backward: recompute
+ * instead of store", folded as m + ln l).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, row-major [B, H, N, d] (batch, heads, sequence,
+ *     head_dim), the layout of "Integration in eight lines"; LSE is [B, H, Nq]
+ *     float32.  Every pointer is DEVICE memory owned by the caller and must
+ *     be 16-byte aligned.  Inputs are only read; outputs are fully
+ *     overwritten (every element, including tail rows); nothing needs to be
+ *     zeroed first.
+ *   - causal != 0 masks future keys ("Causal masking" section) with
+ *     bottom-right alignment: query i sees key j iff j <= i + (Nk - Nq).
+ *     For Nq == Nk this is the usual lower-triangular mask.  causal with
+ *     Nq > Nk is rejected.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.  The library never
+ *     allocates or frees device memory and keeps no mutable global state:
+ *     calls are reentrant and thread-safe.  Asynchronous GPU faults surface
+ *     at the caller's next synchronisation.
+ *   - Every argument is validated before anything is launched.  A negative
+ *     return value means nothing was launched.  There is no silent fallback
+ *     to another algorithm: an unsupported head size or dtype is an error
+ *     (the silent math-path fallback criticised in "Integration in eight
+ *     lines" is exactly what this library refuses to do).
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = -1,     /* null/misaligned pointer, non-positive size, bad scale, causal with Nq > Nk */
+  ATTN_E_UNSUPPORTED = -2, /* head size or dtype outside what is built */
+  ATTN_E_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes() */
+  ATTN_E_HIP = -4          /* a HIP launch error was reported */
+};
+
+/* Storage types of Q, K, V and O. */
+enum { ATTN_BF16 = 0, ATTN_FP16 = 1 };
+
+/*
+ * Bytes of device workspace attn_fwd() needs for these sizes.  Prefill
+ * (Nq > 1) needs none (returns 0).  Decode (Nq == 1) runs split-KV and
+ * needs room for the per-split partial results: B*H*splits*(d+1) floats,
+ * with `splits` chosen by the library (see attn_fwd_decode_splits()).
+ * Returns 0 for invalid sizes as well; attn_fwd() reports those.
+ */
+size_t attn_fwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
+
+/*
+ * Attention forward, bf16 or fp16 storage, fp32 accumulation.
+ *   q   [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,d]   (dtype)
+ *   out [B,H,Nq,d] (dtype), rounded to nearest even from fp32
+ *   lse [B,H,Nq] float32, natural log; may be NULL (not written)
+ *   d in {64, 128}; B, H, Nq, Nk >= 1; scale finite and > 0
+ *   (use 1/sqrt(d) for the usual softmax(Q K^T / sqrt(d)) V).
+ *   workspace: device buffer of at least attn_fwd_workspace_bytes() bytes
+ *   (may be NULL when that is 0).  The workspace is scratch: its contents
+ *   after the call are unspecified.
+ * Nq == 1 dispatches to the split-KV decode kernels (partials over key
+ * ranges, then a log-sum-exp merge); every other Nq runs the tiled prefill
+ * kernel.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count attn_fwd() uses for a decode problem (Nq == 1). */
+int attn_fwd_decode_splits(int B, int H, int Nk, int d);
+
+/*
+ * Split-KV decode with an explicit split count (1 <= num_splits <= 256,
+ * num_splits <= Nk).  Query length is 1: q and out are [B,H,1,d].  Keys are
+ * cut into num_splits contiguous ranges; each range produces a normalised
+ * partial output and its log-sum-exp in `workspace`
+ * (>= attn_decode_workspace_bytes() bytes), and a second kernel merges the
+ * partials: LSE = M + ln sum_s exp(LSE_s - M), O = sum_s exp(LSE_s - LSE) O_s,
+ * which is one application of the running-statistics update of "The Flash
+ * Attention algorithm" to states computed over disjoint key ranges.
+ * causal is accepted and has no effect (the single query is the newest and
+ * sees every key).  dtype: ATTN_BF16 or ATTN_FP16; d in {64, 128}.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int B, int H, int Nk, int d, float scale, int dtype, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Quantisation of bf16 inputs for the quantised forward (token-level INT8
+ * post-training quantisation of Q and K as in the hoodcat.net post
+ * "INT-FlashAttention: an INT8 quantisation architecture compatible with
+ * FlashAttention"; V in OCP FP8 E4M3 with one scale for the whole tensor).
+ *
+ * attn_quantize_rows_i8: x [rows, d] bf16 -> x8 [rows, d] int8 and
+ *   scales [rows] float32 with s = max|row| / 127 and
+ *   x8 = clamp(rint(x / s), -127, 127) (IEEE fp32 division, round half to
+ *   even); an all-zero row gives s = 0 and x8 = 0.  d in {64, 128}.
+ * attn_quantize_e4m3_workspace_bytes / attn_quantize_tensor_e4m3:
+ *   x [n] bf16 -> x8 [n] E4M3FN codes and *scale_out (DEVICE float) with
+ *   s = max|x| / 448 and x8 = E4M3(x / s), round to nearest even,
+ *   saturating at 448.  n >= 1 and a multiple of 8.  The workspace holds
+ *   the partial maxima of the two-pass reduction.
+ */
+int attn_quantize_rows_i8(const void* x, int8_t* x8, float* scales, long rows, int d, void* stream);
+size_t attn_quantize_e4m3_workspace_bytes(long n);
+int attn_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_out, long n,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Quantised attention forward:
+ *   S_ij = (sum_t q8[i,t] k8[j,t]) * q_scale[i] * k_scale[j] * scale,
+ * with the integer dot products accumulated exactly in int32 by int8 MFMA;
+ * P = exp(S - running max) is cast to E4M3 before the P.V product on fp8
+ * MFMA; the row sum l uses the fp32 P; O = (P~ V8) * v_scale / l.
+ *   q8 [B,H,Nq,d] int8, k8 [B,H,Nk,d] int8, v8 [B,H,Nk,d] E4M3 codes,
+ *   q_scale [B,H,Nq], k_scale [B,H,Nk] float32, v_scale DEVICE pointer to
+ *   one float32; out [B,H,Nq,d] bf16; lse [B,H,Nq] float32 or NULL.
+ *   d == 128; causal as above; Nq, Nk >= 1.
+ */
+int attn_fwd_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
+                const float* q_scale, const float* k_scale, const float* v_scale,
+                void* out, float* lse, int B, int H, int Nq, int Nk, int d,
+                float scale, int causal, void* stream);
+
+/*
+ * Test hooks that expose the quantised kernel's own device code:
+ * attn_debug_qk_i32: s[i,j] = sum_t q8[i,t] k8[j,t] for one head
+ *   (q8 [Nq,d], k8 [Nk,d] int8, s [Nq,Nk] int32), through the same int8
+ *   MFMA tile routine as attn_fwd_q8; d == 128.
+ * attn_debug_cvt_e4m3: y[i] = E4M3(x[i]) through the same conversion
+ *   routine attn_quantize_tensor_e4m3 uses (saturating); n even.
+ */
+int attn_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d, void* stream);
+int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream);
+
+/* Static text for a return code. */
+const char* attn_status_str(int status);
+
+/* Static text describing the build: target, kernels, tile sizes. */
+const char* attn_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,123 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects
+bad arguments before launching anything (no GPU needed: every call here
+fails validation on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from flashattention_forward_amd import binding as Bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn_mi355x.h")
+A = 0x10000          # a fake, 16-byte aligned address: never dereferenced (validation fails first)
+MIS = 0x10008        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_api():
+    names = declared_functions()
+    assert "attn_fwd" in names and "attn_fwd_q8" in names and len(names) == len(Bd.SIGNATURES)
+    assert set(names) == set(Bd.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = Bd.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {Bd.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def fwd(**kw):
+    a = dict(q=A, k=A, v=A, out=A, lse=A, B=1, H=1, Nq=4, Nk=4, d=64, scale=0.125, causal=0, dtype=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return Bd.lib().attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                             a["scale"], a["causal"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), Bd.ATTN_E_INVALID), (dict(v=None), Bd.ATTN_E_INVALID), (dict(out=None), Bd.ATTN_E_INVALID),
+    (dict(k=MIS), Bd.ATTN_E_INVALID), (dict(lse=A + 2), Bd.ATTN_E_INVALID),
+    (dict(B=0), Bd.ATTN_E_INVALID), (dict(H=-1), Bd.ATTN_E_INVALID), (dict(Nq=0), Bd.ATTN_E_INVALID),
+    (dict(Nk=0), Bd.ATTN_E_INVALID),
+    (dict(scale=0.0), Bd.ATTN_E_INVALID), (dict(scale=-1.0), Bd.ATTN_E_INVALID),
+    (dict(scale=float("nan")), Bd.ATTN_E_INVALID), (dict(scale=float("inf")), Bd.ATTN_E_INVALID),
+    (dict(causal=1, Nq=5, Nk=4), Bd.ATTN_E_INVALID),
+    (dict(B=2 ** 20, H=2 ** 20), Bd.ATTN_E_INVALID),
+    (dict(d=96), Bd.ATTN_E_UNSUPPORTED), (dict(d=256), Bd.ATTN_E_UNSUPPORTED), (dict(dtype=2), Bd.ATTN_E_UNSUPPORTED),
+    (dict(Nq=1, ws=None, wsb=0), Bd.ATTN_E_WORKSPACE), (dict(Nq=1, ws=A, wsb=16), Bd.ATTN_E_WORKSPACE),
+    (dict(Nq=1, ws=MIS, wsb=1 << 20), Bd.ATTN_E_WORKSPACE),
+])
+def test_attn_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_workspace_sizes():
+    L = Bd.lib()
+    assert L.attn_fwd_workspace_bytes(4, 32, 4096, 4096, 128, 0) == 0
+    s = L.attn_fwd_decode_splits(64, 32, 8192, 128)
+    assert 1 <= s <= 256
+    assert L.attn_fwd_workspace_bytes(64, 32, 1, 8192, 128, 0) == 64 * 32 * s * 129 * 4
+    assert L.attn_decode_workspace_bytes(2, 3, 64, 5) == 2 * 3 * 5 * 65 * 4
+    assert L.attn_decode_workspace_bytes(2, 3, 96, 5) == 0
+    assert L.attn_fwd_workspace_bytes(1, 1, 1, 1, 96, 0) == 0
+    # small problems still split into several ranges only while each keeps >= 128 keys
+    assert L.attn_fwd_decode_splits(1, 1, 100, 128) == 1
+
+
+def test_decode_rejects():
+    L = Bd.lib()
+    args = lambda ns, ws, wsb, d=128, dt=0: L.attn_fwd_decode(A, A, A, A, A, 2, 2, 64, d, 0.1, dt, ns, ws, wsb, None)
+    assert args(0, A, 1 << 20) == Bd.ATTN_E_INVALID
+    assert args(65, A, 1 << 20) == Bd.ATTN_E_INVALID      # more splits than keys
+    assert args(257, A, 1 << 20) == Bd.ATTN_E_INVALID
+    assert args(4, None, 0) == Bd.ATTN_E_WORKSPACE
+    assert args(4, A, L.attn_decode_workspace_bytes(2, 2, 128, 4) - 1) == Bd.ATTN_E_WORKSPACE
+    assert args(4, A, 1 << 20, d=80) == Bd.ATTN_E_UNSUPPORTED
+    assert args(4, A, 1 << 20, dt=7) == Bd.ATTN_E_UNSUPPORTED
+
+
+def test_quant_entry_points_reject():
+    L = Bd.lib()
+    q8 = lambda **kw: L.attn_fwd_q8(kw.get("q", A), A, A, kw.get("qs", A), A, kw.get("vs", A), A, None, 1, 1,
+                                    kw.get("Nq", 8), 8, kw.get("d", 128), kw.get("scale", 0.1),
+                                    kw.get("causal", 0), None)
+    assert q8(d=64) == Bd.ATTN_E_UNSUPPORTED
+    assert q8(qs=None) == Bd.ATTN_E_INVALID
+    assert q8(vs=None) == Bd.ATTN_E_INVALID
+    assert q8(q=None) == Bd.ATTN_E_INVALID
+    assert q8(Nq=9, causal=1) == Bd.ATTN_E_INVALID
+    assert q8(scale=float("nan")) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_rows_i8(A, A, A, 10, 96, None) == Bd.ATTN_E_UNSUPPORTED
+    assert L.attn_quantize_rows_i8(A, A, A, 0, 128, None) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_rows_i8(MIS, A, A, 4, 128, None) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_e4m3_workspace_bytes(12) == 0
+    assert L.attn_quantize_e4m3_workspace_bytes(1 << 20) > 0
+    assert L.attn_quantize_tensor_e4m3(A, A, A, 12, A, 4096, None) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_tensor_e4m3(A, A, A, 1 << 20, A, 4, None) == Bd.ATTN_E_WORKSPACE
+    assert L.attn_quantize_tensor_e4m3(A, A, A, 1 << 20, None, 1 << 20, None) == Bd.ATTN_E_WORKSPACE
+    assert L.attn_debug_qk_i32(A, A, A, 4, 4, 64, None) == Bd.ATTN_E_UNSUPPORTED
+    assert L.attn_debug_qk_i32(None, A, A, 4, 4, 128, None) == Bd.ATTN_E_INVALID
+    assert L.attn_debug_cvt_e4m3(A, A, 3, None) == Bd.ATTN_E_INVALID
+
+
+def test_status_strings_and_build_info():
+    for c in (0, -1, -2, -3, -4):
+        assert Bd.status_str(c) and Bd.status_str(c) != "unknown status"
+    assert Bd.status_str(99) == "unknown status"
+    assert "gfx950" in Bd.build_info()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(Bd, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(Bd, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        Bd.lib()

@@ -1,0 +1,150 @@
+"""GPU parity of the quantised path: the quantisation kernels and the int32
+score accumulators are bit-exact against the oracle's emulation; the
+quantised forward meets max |O - O_ref| <= 5e-2 against the oracle that
+emulates the same quantisation."""
+import numpy as np
+import pytest
+
+import fa_inputs as G
+from oracle import quant as Q
+
+pytestmark = pytest.mark.gpu
+
+QO_TOL, LSE_TOL = 5e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def F():
+    import torch
+    import flashattention_forward_amd as F
+    assert torch.cuda.is_available()
+    F.lib()
+    return F
+
+
+def test_qk_int32_bit_exact(F):
+    """int32 Q8 K8^T from the kernel's own MFMA tile routine equals exact
+    integer products, including the extreme +-127 rows and ragged tiles."""
+    import torch
+    rng = np.random.default_rng(60)
+    for (Nq, Nk) in [(128, 64), (300, 200), (77, 513)]:
+        q8 = rng.integers(-127, 128, (Nq, 128)).astype(np.int8)
+        k8 = rng.integers(-127, 128, (Nk, 128)).astype(np.int8)
+        q8[0] = 127
+        k8[0] = -127
+        k8[1] = 127
+        print(f"  gpu: debug_qk_i32 Nq={Nq} Nk={Nk}", flush=True)
+        s = F.debug_qk_i32(torch.from_numpy(q8).cuda(), torch.from_numpy(k8).cuda())
+        torch.cuda.synchronize()
+        ref = Q.qk_int(q8, k8)
+        assert np.array_equal(s.cpu().numpy().astype(np.int64), ref)
+        assert ref[0, 0] == -127 * 127 * 128 and ref[0, 1] == 127 * 127 * 128
+
+
+def test_e4m3_conversion_bit_exact(F):
+    """The library's fp32 -> E4M3 conversion equals the oracle's encoding on
+    every grid point, every midpoint (ties to even), their fp32 neighbours,
+    the subnormal range and the saturating range."""
+    import torch
+    from tests.oracle_pins import _e4m3_sweep
+    x = _e4m3_sweep()
+    x = np.concatenate([x, np.array([448.0, 460.0, 464.0, 470.0, 1e4, -1e4, 0.0, -0.0], np.float32)])
+    if x.size % 2:
+        x = np.append(x, np.float32(1.0))
+    print(f"  gpu: debug_cvt_e4m3 n={x.size}", flush=True)
+    y = F.debug_cvt_e4m3(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    ref = Q.e4m3_encode(x)
+    bad = np.nonzero(y.cpu().numpy() != ref)[0]
+    assert bad.size == 0, (x[bad[:5]], y.cpu().numpy()[bad[:5]], ref[bad[:5]])
+
+
+def _quantize_on_gpu(F, q, k, v):
+    import torch
+    from tests.gpu_util import to_dev
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    q8, sq = F.quantize_rows_i8(tq)
+    k8, sk = F.quantize_rows_i8(tk)
+    v8, sv = F.quantize_tensor_e4m3(tv)
+    torch.cuda.synchronize()
+    return q8, sq, k8, sk, v8, sv
+
+
+def _check_quantisation(qi, q8, sq, k8, sk, v8, sv):
+    assert np.array_equal(q8.cpu().numpy(), qi["q8"])
+    assert np.array_equal(sq.cpu().numpy(), qi["sq"])
+    assert np.array_equal(k8.cpu().numpy(), qi["k8"])
+    assert np.array_equal(sk.cpu().numpy(), qi["sk"])
+    assert np.array_equal(v8.cpu().numpy(), qi["v8"])
+    assert sv.cpu().numpy()[0] == qi["sv"]
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 2, 300, 300), False), ((2, 1, 77, 333), True),
+                                          ((1, 1, 128, 64), False), ((1, 2, 200, 1000), False),
+                                          ((1, 1, 260, 260), True)],
+                         ids=lambda x: str(x))
+def test_q8_small(F, shape, causal):
+    import torch
+    from tests.gpu_util import errors, from_dev
+    B, H, Nq, Nk = shape
+    w = G.Workload("q8_small", 61, B, H, Nq, Nk, 128, "bf16", 1.0, causal, 128 ** -0.5)
+    q, k, v = G.draw_qkv(w)
+    f32 = lambda x: G.to_f32(x, "bf16")
+    O, L, qi = Q.attention_q8(f32(q), f32(k), f32(v), w.scale, causal)
+    q8, sq, k8, sk, v8, sv = _quantize_on_gpu(F, q, k, v)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    print(f"  gpu: attn_fwd_q8 {shape} causal={causal}", flush=True)
+    out, lse = F.attn_fwd_q8(q8, k8, v8, sq, sk, sv, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    eo, ro = errors(from_dev(out), O)
+    el, _ = errors(from_dev(lse), L)
+    print(f"  max|dO|={eo:.3e} (rel {ro:.3e}) max|dLSE|={el:.3e}", flush=True)
+    assert eo <= QO_TOL and el <= LSE_TOL
+
+
+def test_q8_zero_rows(F):
+    """An all-zero Q row quantises to scale 0 and attends uniformly; an
+    all-zero K row gets scale 0 and score 0."""
+    import torch
+    from tests.gpu_util import from_dev, to_dev
+    w = G.Workload("q8_zero", 62, 1, 1, 130, 70, 128, "bf16", 1.0, False, 128 ** -0.5)
+    q, k, v = G.draw_qkv(w)
+    q[0, 0, 5] = 0
+    k[0, 0, 3] = 0
+    f32 = lambda x: G.to_f32(x, "bf16")
+    O, L, qi = Q.attention_q8(f32(q), f32(k), f32(v), w.scale)
+    assert qi["sq"][0, 0, 5] == 0 and qi["sk"][0, 0, 3] == 0
+    q8, sq, k8, sk, v8, sv = _quantize_on_gpu(F, q, k, v)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    out, lse = F.attn_fwd_q8(q8, k8, v8, sq, sk, sv, scale=w.scale)
+    torch.cuda.synchronize()
+    assert np.abs(from_dev(out) - O).max() <= QO_TOL and np.abs(from_dev(lse) - L).max() <= LSE_TOL
+
+
+def test_q8_full_size_sampled(F):
+    """B=2 H=32 N=8192 d=128: whole-tensor quantisation bit-exact; the
+    quantised forward over all heads, sampled rows of sampled heads checked."""
+    import torch
+    from tests.gpu_util import from_dev
+    w = G.WORKLOADS["quant_8k"]
+    q, k, v = G.draw_qkv(w, threads=16)
+    f32 = lambda x: G.to_f32(x, "bf16")
+    qi = Q.quantize_inputs(f32(q), f32(k), f32(v))
+    q8, sq, k8, sk, v8, sv = _quantize_on_gpu(F, q, k, v)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    print("  gpu: attn_fwd_q8 full size", flush=True)
+    out, lse = F.attn_fwd_q8(q8, k8, v8, sq, sk, sv, scale=w.scale)
+    torch.cuda.synchronize()
+    o_all, l_all = from_dev(out), from_dev(lse)
+    assert np.isfinite(o_all).all() and np.isfinite(l_all).all()
+    rng = np.random.default_rng(3)
+    worst = 0.0
+    for bh in rng.choice(w.B * w.H, 5, replace=False):
+        b, h = divmod(int(bh), w.H)
+        rows = np.unique(np.concatenate([[0, 8191], rng.integers(0, w.Nq, 40)]))
+        O, L = Q.attention_q8_head(qi["q8"][b, h][rows], qi["sq"][b, h][rows], qi["k8"][b, h], qi["sk"][b, h],
+                                   qi["v8"][b, h], qi["sv"], w.scale)
+        worst = max(worst, np.abs(o_all[b, h, rows] - O).max())
+        assert np.abs(l_all[b, h, rows] - L).max() <= LSE_TOL
+    print(f"  sampled max|dO|={worst:.3e}", flush=True)
+    assert worst <= QO_TOL
