@@ -1,0 +1,234 @@
+"""Benchmark of the MI355X FlashAttention forward (one GPU).
+
+One step = the prefill workload B=4, H=32, N=4096, d=128, bf16 Q/K/V drawn
+i.i.d. N(0,1), scale 1/sqrt(128), run once non-causal and once causal (one
+launch each).  `value` is algorithmic TFLOP/s over the step: 4*B*H*N^2*d
+FLOPs non-causal plus half of that causal, divided by the measured time,
+with inputs resident in device memory before the timed region.
+
+Printed as ONE JSON line, which also carries
+  * roofline: the dominant kernel (non-causal prefill), its algorithmic
+    FLOPs per launch over its average launch time (HIP events on its stream)
+    against the dense bf16 MFMA peak, and the HBM traffic per launch taken
+    from committed rocprofv3 counter runs when they match the current kernel
+    source (null otherwise);
+  * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
+    workload on this host's cores;
+  * other_workloads: the long causal fp16 sequence, the split-KV decode
+    (GB/s over the K+V bytes) and the quantised forward, each timed the same
+    way (informational).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % MFMA peak (prefill); HBM GB/s & % peak (decode)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # dense fp8 / int8
+PEAK_HBM_GBS = 8000.0         # HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4k_traffic.json")
+KERNEL_SOURCES = ["flashattention_forward_amd/csrc/prefill.hip", "flashattention_forward_amd/csrc/common.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per launch of the non-causal prefill kernel from the committed
+    counter runs, or None if they were taken on another kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed_launches(fns, steps, warmup):
+    """Run the list of launch closures `steps` times after `warmup` rounds;
+    returns (total seconds, [average seconds per launch of each closure])."""
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            ev[s][i][0].record()
+            f()
+            ev[s][i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1) / 1e3
+    per = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps / 1e3 for i in range(len(fns))]
+    return total, per
+
+
+def cpu_baseline(seconds_target: float = 15.0):
+    """The fp64 oracle on a bounded sample of the prefill workload: whole
+    heads, alternating non-causal and causal, until ~seconds_target."""
+    import numpy as np
+    import fa_inputs as G
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = G.WORKLOADS["prefill_4k"]
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds_target and heads < 64:
+        b, h = divmod(heads, w.H)
+        q, k, v = (G.to_f64(x[0], "bf16") for x in G.draw_qkv(w, heads=[(b, h)]))
+        causal = bool(heads % 2)
+        A.attention_head(q, k, v, w.scale, causal)
+        flops += 4.0 * w.Nq * w.Nk * w.d / (2.0 if causal else 1.0)
+        heads += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} whole heads (alternating non-causal/causal) of B=4 H=32 N=4096 d=128 bf16, "
+                      f"fp64 numpy, {dt:.1f} s incl. input generation"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (attention shards by (batch, head) "
+              "with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import fa_inputs as G
+    import flashattention_forward_amd as F
+
+    F.lib()
+    torch.cuda.set_device(0)
+    w = G.WORKLOADS["prefill_4k"]
+    q, k, v = (G.to_torch(x, "bf16") for x in G.draw_qkv(w, threads=16))
+    out_nc, out_c = torch.empty_like(q), torch.empty_like(q)
+    lse_nc = torch.empty((w.B, w.H, w.Nq), device="cuda")
+    lse_c = torch.empty_like(lse_nc)
+    flops_nc = G.WORKLOADS["prefill_4k"].flops()
+    flops_c = G.WORKLOADS["prefill_4k_causal"].flops()
+    fns = [lambda: F.attn_fwd(q, k, v, causal=False, scale=w.scale, out=out_nc, lse=lse_nc),
+           lambda: F.attn_fwd(q, k, v, causal=True, scale=w.scale, out=out_c, lse=lse_c)]
+    total, per = timed_launches(fns, args.steps, args.warmup)
+    value = (flops_nc + flops_c) * args.steps / total / 1e12
+    achieved = flops_nc / per[0] / 1e12
+    traffic = traffic_per_launch()
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1), rounded to bf16)",
+        "config": {"workload": "prefill_4k: B=4 H=32 Nq=Nk=4096 d=128 bf16, scale 1/sqrt(128); one step = one "
+                               "non-causal + one causal launch", "global_batch": w.B, "seq_len": w.Nq,
+                   "heads": w.H, "head_dim": w.d, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "prefill_kernel<128, bf16, non-causal>",
+                     "flops_per_launch": flops_nc},
+        "kernels": {
+            "prefill_noncausal": {"ms": round(per[0] * 1e3, 4), "tflops": round(flops_nc / per[0] / 1e12, 3),
+                                  "frac_peak": round(flops_nc / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "prefill_causal": {"ms": round(per[1] * 1e3, 4), "tflops": round(flops_c / per[1] / 1e12, 3),
+                               "frac_peak": round(flops_c / per[1] / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        },
+    }
+    del q, k, v, out_nc, out_c, lse_nc, lse_c
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        other = {}
+        # long causal sequence, fp16 d=64
+        wl = G.WORKLOADS["long_23400_causal"]
+        tq, tk, tv = (G.to_torch(x, "fp16") for x in G.draw_qkv(wl, threads=16))
+        o = torch.empty_like(tq)
+        l = torch.empty((wl.B, wl.H, wl.Nq), device="cuda")
+        _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, causal=True, scale=wl.scale, out=o, lse=l)],
+                                max(5, args.steps // 2), args.warmup)
+        other["long_23400_causal"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(wl.flops() / per[0] / 1e12, 3),
+                                      "frac_peak": round(wl.flops() / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del tq, tk, tv, o, l
+        # split-KV decode
+        wd = G.WORKLOADS["decode_8k"]
+        tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(wd, threads=16))
+        o = torch.empty_like(tq)
+        l = torch.empty((wd.B, wd.H, 1), device="cuda")
+        splits = F.decode_splits(wd.B, wd.H, wd.Nk, wd.d)
+        ws = torch.empty(F.workspace_bytes(wd.B, wd.H, 1, wd.Nk, wd.d, 0), device="cuda", dtype=torch.uint8)
+        _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, scale=wd.scale, out=o, lse=l, workspace=ws)],
+                                args.steps, args.warmup)
+        kv_bytes = 2 * wd.B * wd.H * wd.Nk * wd.d * 2
+        other["decode_8k"] = {"ms": round(per[0] * 1e3, 4), "splits": splits,
+                              "gbs_kv": round(kv_bytes / per[0] / 1e9, 1),
+                              "frac_hbm_peak": round(kv_bytes / per[0] / 1e9 / PEAK_HBM_GBS, 4),
+                              "kv_bytes": kv_bytes}
+        del tq, tk, tv, o, l, ws
+        torch.cuda.empty_cache()
+        # quantised forward (timing covers attn_fwd_q8 only; quantisation reported apart)
+        wq = G.WORKLOADS["quant_8k"]
+        tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(wq, threads=16))
+        q8, sq = F.quantize_rows_i8(tq)
+        k8, sk = F.quantize_rows_i8(tk)
+        v8, sv = F.quantize_tensor_e4m3(tv)
+        o = torch.empty((wq.B, wq.H, wq.Nq, wq.d), device="cuda", dtype=torch.bfloat16)
+        l = torch.empty((wq.B, wq.H, wq.Nq), device="cuda")
+        _, per = timed_launches([lambda: F.attn_fwd_q8(q8, k8, v8, sq, sk, sv, scale=wq.scale, out=o, lse=l)],
+                                args.steps, args.warmup)
+        _, perq = timed_launches([lambda: (F.quantize_rows_i8(tq), F.quantize_rows_i8(tk),
+                                           F.quantize_tensor_e4m3(tv))], 5, 1)
+        ops = wq.flops()
+        other["quant_8k"] = {"ms": round(per[0] * 1e3, 4), "tops": round(ops / per[0] / 1e12, 3),
+                             "frac_fp8_peak": round(ops / per[0] / 1e12 / PEAK_FP8_TFLOPS, 4),
+                             "quantize_ms": round(perq[0] * 1e3, 4)}
+        del tq, tk, tv, q8, k8, v8, sq, sk, sv, o, l
+        torch.cuda.empty_cache()
+        res["other_workloads"] = other
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

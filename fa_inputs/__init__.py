@@ -143,3 +143,14 @@ def draw_qkv(w: Workload, seed: int = 0, heads=None, threads: int = 8):
 def shrink(w: Workload, **kw) -> Workload:
     """A smaller workload with the same distribution and a new name/id mix."""
     return dataclasses.replace(w, **kw)
+
+
+def to_torch(x: np.ndarray, dtype: str, device: str = "cuda"):
+    """A stored tensor (bf16 bits as uint16, or fp16) as a torch tensor of
+    that dtype on ``device`` (a bit-for-bit copy)."""
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "fp16":
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    raise ValueError(dtype)

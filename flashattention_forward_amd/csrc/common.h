@@ -89,8 +89,35 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* base, uint32_t byte_of
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((ATTN_LDS i32x2*)((ATTN_LDS char*)(base) + byte_off));
 }
 
-// Exchange between lane l and lane l ^ 32.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+// Reductions over the lane pair (l, l ^ 32) with v_permlane32_swap: the two
+// results of the swap are the lane's own value and its partner's (in some
+// order), so a symmetric operation on them is the pair reduction.
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)s[0]), __builtin_bit_cast(float, (unsigned)s[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
+}
+
+// ---------------------------------------------------------------- buffers
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets at or
+// beyond `bytes` return zero (hardware range check), which is how the
+// kernels read tail rows without branches.  Offsets are 32-bit, so one
+// resource covers less than 2 GiB (checked on the host).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// scheduling-group masks for __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100, kSchedDsWrite = 0x200,
+              kSchedVmemRead = 0x020;
 
 // ---------------------------------------------------------------- grid order
 // Workgroups are handed to the 8 XCDs round robin (id % 8).  Renumber them so

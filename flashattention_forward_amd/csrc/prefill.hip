@@ -44,19 +44,26 @@ namespace attn {
 
 template <int D>
 struct PrefillCfg {
-  static constexpr int BM = 128;              // query rows per workgroup
-  static constexpr int BN = 64;               // keys per tile
-  static constexpr int NT = 256;              // threads (4 waves)
-  static constexpr int KSTRIDE = D * 2 + 16;  // LDS bytes per K row
-  static constexpr int VSTRIDE = D * 2 + 64;  // LDS bytes per V row
-  static constexpr int KBYTES = BN * KSTRIDE;
-  static constexpr int VBYTES = BN * VSTRIDE;
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int RPP = NT / CPR;        // rows per staging pass
-  static constexpr int PASSES = BN / RPP;
-  static constexpr int KSTEPS = D / 16;       // k-steps of S^T = K Q^T
-  static constexpr int MB_O = D / 32;         // 32-row blocks of O^T
+  static constexpr int BM = 128;             // query rows per workgroup
+  static constexpr int BN = 64;              // keys per tile
+  static constexpr int NT = 256;             // threads (4 waves)
+  static constexpr int ROWB = D * 2;         // bytes per K/V row
+  static constexpr int SPR = ROWB / 16;      // 16-byte slots per row
+  static constexpr int TILEB = BN * ROWB;    // bytes per K or V tile in LDS
+  static constexpr int RPI = 1024 / ROWB;    // rows per 1 KB direct-to-LDS wave load
+  static constexpr int LPW = TILEB / 1024 / 4;  // such loads per wave per tile
+  static constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
+  static constexpr int MB_O = D / 32;        // 32-row blocks of O^T
 };
+
+// LDS swizzles (16-byte slot index XOR a function of the row), chosen so the
+// MFMA operand reads of a wave hit distinct banks.  K: 16 lanes read one slot
+// of 16 consecutive rows; V: 16-lane groups read 32 bytes of 4 consecutive
+// rows for the transposing read.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // Raise the running max only when a tile exceeds it by more than this
 // (log2 units): P = exp2(s - m) then stays below 2^8.
@@ -72,9 +79,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   using M = Mfma<BF16>;
   typedef typename M::op8 op8;
   typedef typename M::op2 op2;
-  __shared__ __attribute__((aligned(16))) char smem[C::KBYTES + C::VBYTES];
-  char* lk = smem;
-  char* lv = smem + C::KBYTES;
+  constexpr int NA = 2 * C::KSTEPS;  // MFMAs of S^T per tile (2 key blocks x k-steps)
+  constexpr int NC = 4 * C::MB_O;    // MFMAs of O^T per tile (4 16-key steps x d blocks)
+  // two K and two V tile buffers: tile t+1's K and tile t's V are read while
+  // tile t+2's K and tile t+1's V arrive
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILEB];
 
   const int logical = xcd_remap(blockIdx.x, total);
   const int bh = logical / nqb;
@@ -87,47 +96,78 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int h = lane >> 5, l32 = lane & 31;
   const size_t qbase = (size_t)bh * Nq * D;
   const size_t kbase = (size_t)bh * Nk * D;
+  const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
+  const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
+  const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
 
-  // B operand of S^T = K Q^T: lane holds Q[qrow][16kk + 8h .. +7].
+  // B operand of S^T = K Q^T: lane holds Q[qrow][16kk + 8h .. +7]; rows past Nq read as 0
   const int qrow = q0 + 32 * w + l32;
   op8 qop[C::KSTEPS];
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(Q + qbase + (size_t)qrow * D);
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < Nq) x = src[2 * kk + h];
-      qop[kk] = __builtin_bit_cast(op8, x);
-    }
-  }
+  for (int kk = 0; kk < C::KSTEPS; ++kk)
+    qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)qrow * C::ROWB + (16 * kk + 8 * h) * 2));
+  // keep the Q loads ahead of the first tile's: the in-order load counter then
+  // retires them before the first tile is read, and no wait on them lands in the loop
+  __builtin_amdgcn_sched_barrier(0);
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
-  // register staging of one K/V tile
-  u32x4 kreg[C::PASSES], vreg[C::PASSES];
-  auto gload = [&](int t) {
-    const int kv0 = t * C::BN;
+  // direct global -> LDS loads of one tile: wave w fills 1 KB blocks
+  // LPW*w .. LPW*w + LPW-1; lane i lands at byte 16 i of its block (row i/SPR,
+  // slot i%SPR) and therefore fetches global chunk slot ^ swizzle(row).
+  // Keys past Nk read as 0 (buffer range check).
+  char* kb[2] = {smem, smem + C::TILEB};
+  char* vb[2] = {smem + 2 * C::TILEB, smem + 3 * C::TILEB};
+  uint32_t gk_off[C::LPW], gv_off[C::LPW];
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int row = p * C::RPP + tid / C::CPR, ch = tid % C::CPR;
-      const int key = kv0 + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (key < Nk) {
-        a = reinterpret_cast<const u32x4*>(K + kbase + (size_t)key * D)[ch];
-        b = reinterpret_cast<const u32x4*>(V + kbase + (size_t)key * D)[ch];
-      }
-      kreg[p] = a;
-      vreg[p] = b;
-    }
+  for (int i = 0; i < C::LPW; ++i) {
+    const int blk = C::LPW * w + i;
+    const int row = blk * C::RPI + lane / C::SPR, slot = lane % C::SPR;
+    gk_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ k_swz<D>(row));
+    gv_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ v_swz<D>(row));
+  }
+  auto load_tile = [&](const __amdgpu_buffer_rsrc_t& r, const uint32_t* goff, char* dst, int t) {
+    const uint32_t toff = (uint32_t)t * (C::BN * C::ROWB);
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)(dst + 1024 * (C::LPW * w + i)), 16,
+                                               toff + goff[i], 0, 0, 0);
   };
-  auto lstore = [&]() {
+  // per-lane LDS operand offsets (constant across tiles)
+  uint32_t ka_off[C::KSTEPS];  // K operand, row l32 (+32 per key block), logical slot 2kk+h
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int row = p * C::RPP + tid / C::CPR, ch = tid % C::CPR;
-      lds_store<u32x4>(lk, row * C::KSTRIDE + ch * 16, kreg[p]);
-      lds_store<u32x4>(lv, row * C::VSTRIDE + ch * 16, vreg[p]);
+  for (int kk = 0; kk < C::KSTEPS; ++kk) ka_off[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ k_swz<D>(l32));
+  const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+  const int vrow = (r16 >> 2) + 4 * h;  // + 16 per key group, + 8 for the second read
+  uint32_t va_off[C::MB_O];            // V^T operand: columns 32mb + 16g1 + 4(r16&3)
+#pragma unroll
+  for (int mb = 0; mb < C::MB_O; ++mb) {
+    const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
+    va_off[mb] = vrow * C::ROWB + 16 * ((col >> 3) ^ v_swz<D>(vrow)) + 2 * (col & 7);
+  }
+  auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i&1, k-step i>>1
+    return lds_load<op8>(lk, ka_off[i >> 1] + (i & 1) * 32 * C::ROWB);
+  };
+  auto va_load = [&](const char* lv, int j) {  // V^T operand of O^T step j: 16-key group j/MB_O, d block j%MB_O
+    const uint32_t a0 = va_off[j % C::MB_O] + 16 * (j / C::MB_O) * C::ROWB;
+    const s16x4 lo = lds_read_tr16(lv, a0);
+    const s16x4 hi = lds_read_tr16(lv, a0 + 8 * C::ROWB);
+    return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // S^T of one tile from the K tile in LDS (2 accumulators interleaved)
+  auto qk_tile = [&](const char* lk, f32x16* s) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    op8 ka[2];
+    ka[0] = ka_load(lk, 0);
+    ka[1] = ka_load(lk, 1);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const op8 a = ka[i & 1];
+      if (i + 2 < NA) ka[i & 1] = ka_load(lk, i + 2);
+      s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
     }
   };
 
@@ -137,98 +177,116 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   const int qmin_w = q0 + 32 * w;  // smallest query row of this wave
 
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gload(t + 1);
+  // -inf on keys past Nk and (causal) on keys in a row's future; only tiles
+  // that hold such keys take this path
+  auto mask_tile = [&](int t, f32x16* s) {
     const int kv0 = t * C::BN;
-    // whole tile in this wave's future: nothing to add
-    const bool skip = CAUSAL && (kv0 > qmin_w + 31 + off);
-    if (!skip) {
-      // ---- S^T = K Q^T  (two 32-key blocks)
-      f32x16 s[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        s[nb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < C::KSTEPS; ++kk) {
-          const op8 a = lds_load<op8>(lk, (32 * nb + l32) * C::KSTRIDE + (16 * kk + 8 * h) * 2);
-          s[nb] = M::mma(a, qop[kk], s[nb]);
-        }
-      }
-      // ---- masks: key tail, causal diagonal
-      const bool need_mask = (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
-      if (need_mask) {
-        const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
-          }
-      }
-      // ---- row max over the tile (this lane's 32 keys, then the other half-wave)
-      float mx = s[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mt = mx * c;
-      if (__any(mt > m_run + kRescaleThreshold)) {
-        const float mn = fmaxf(m_run, mt);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-#pragma unroll
-        for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
-        l_run *= alpha;
-        m_run = mn;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      // ---- P = exp2(s*c - m), packed to 16-bit B operands; l sums the fp32 P
-      op8 pb[2][2];
+    if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
+      const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          op2 pr[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j], c, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use));
-            pr[j] = M::pack2(p0, p1);
-            l_run += p0 + p1;
-          }
-          pb[nb][tt] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                               __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
-                                               0, 1, 2, 3, 4, 5, 6, 7);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
         }
-      // ---- O^T += V^T P^T
-      const int r16 = lane & 15, g1 = (lane >> 4) & 1;
-#pragma unroll
-      for (int mb = 0; mb < C::MB_O; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int key0 = 32 * nb + 16 * tt + 4 * h;
-            const uint32_t a0 = (key0 + (r16 >> 2)) * C::VSTRIDE + (32 * mb + 16 * g1 + 4 * (r16 & 3)) * 2;
-            const s16x4 lo = lds_read_tr16(lv, a0);
-            const s16x4 hi = lds_read_tr16(lv, a0 + 8 * C::VSTRIDE);
-            const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[mb] = M::mma(__builtin_bit_cast(op8, a), pb[nb][tt], o[mb]);
-          }
     }
+  };
+  // running-max update for a tile: the max only moves when the tile's max
+  // exceeds it by more than the threshold (wave-uniform decision)
+  bool rescale;
+  float alpha;
+  auto tile_stats = [&](const f32x16* s, bool commit) {
+    float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) {
+      mx0 = fmaxf(mx0, s[0][i]);
+      mx1 = fmaxf(mx1, s[1][i]);
+    }
+    const float mt = pair_max(fmaxf(mx0, mx1)) * c;
+    const bool r = __any(mt > m_run + kRescaleThreshold) && commit;
+    const float m_new = r ? fmaxf(m_run, mt) : m_run;
+    alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    rescale = r;
+    m_run = m_new;
+  };
+
+  // prologue: K(0), V(0), K(1) into LDS; S(0) and its statistics
+  load_tile(rk, gk_off, kb[0], 0);
+  load_tile(rv, gv_off, vb[0], 0);
+  if (ntiles > 1) load_tile(rk, gk_off, kb[1], 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk_tile(kb[0], sa);
+  __syncthreads();  // every wave is done with K(0) before iteration 0 overwrites it
+  mask_tile(0, sa);
+  tile_stats(sa, true);
+
+  // one tile: the softmax of S(t) (statistics already known) overlaps the
+  // MFMAs of S(t+1); the MFMAs of O += P(t) V(t) overlap the row max of S(t+1)
+  auto step = [&](int t, f32x16* s_cur, f32x16* s_nxt) {
+    const bool has_next = t + 1 < ntiles;
+    if (t + 2 < ntiles) load_tile(rk, gk_off, kb[t & 1], t + 2);
+    if (has_next) load_tile(rv, gv_off, vb[(t + 1) & 1], t + 1);
+    if (rescale) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // region A: S(t+1) on the MFMA (on the last tile this reads a stale buffer
+    // and the result is dropped), P(t) on the VALU
+    qk_tile(kb[(t + 1) & 1], s_nxt);
+    op8 pb[4];
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nb = g >> 1, tt = g & 1;
+      op2 pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[nb][8 * tt + 2 * j], c, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[nb][8 * tt + 2 * j + 1], c, -m_use));
+        pr[j] = M::pack2(p0, p1);
+        lsum[j] += p0 + p1;
+      }
+      pb[g] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                      __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    l_run = fmaf(l_run, alpha, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+    // interleave: each MFMA of S(t+1) with its next operand read and a share of the softmax
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 120 / NA, 0);
+    }
+    // keep P(t) in region A (otherwise it is sunk next to its MFMA uses)
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run));
+    if (has_next) mask_tile(t + 1, s_nxt);
+    // region B: O^T += V(t)^T P(t)^T on the MFMA, statistics of S(t+1) on the VALU
+    const char* lv = vb[t & 1];
+    op8 va[3];
+    va[0] = va_load(lv, 0);
+    va[1] = va_load(lv, 1);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const op8 a = va[j % 3];
+      if (j + 2 < NC) va[(j + 2) % 3] = va_load(lv, j + 2);
+      o[j % C::MB_O] = M::mma(a, pb[j / C::MB_O], o[j % C::MB_O]);
+    }
+    tile_stats(s_nxt, has_next);
+    // the loads of K(t+2) and V(t+1) have landed in every wave's part of LDS
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) {
-      lstore();
-      __syncthreads();
-    }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < ntiles) step(t + 1, sb, sa);
   }
 
   // ---- epilogue: combine the half-wave row sums, normalise, write O and LSE
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = 1.f / l_tot;
   if (qrow < Nq) {
     uint16_t* dst = O + qbase + (size_t)qrow * D;

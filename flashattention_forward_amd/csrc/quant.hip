@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
-      mt = fmaxf(mt, swap_halves(mt));
+      mt = pair_max(mt);
       if (__any(mt > m_run + kRescaleThresholdQ)) {
         const float mn = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
     }
   }
 
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   const float f = *VS / l_tot;
   if (qrow < Nq) {
     uint16_t* dst = O + (qbase + qrow) * C::D;

@@ -8,11 +8,7 @@ import fa_inputs as G
 
 def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
     """Stored tensor (bf16 bits as uint16, or fp16) -> GPU tensor."""
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
-    if dtype == "fp16":
-        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    raise ValueError(dtype)
+    return G.to_torch(x, dtype, "cuda")
 
 
 def from_dev(t: torch.Tensor) -> np.ndarray:
