@@ -44,16 +44,19 @@ namespace attn {
 
 template <int D>
 struct PrefillCfg {
-  static constexpr int BM = 128;             // query rows per workgroup
+  static constexpr int BM = 256;             // query rows per workgroup: 2 groups x 4 waves x 32
   static constexpr int BN = 64;              // keys per tile
-  static constexpr int NT = 256;             // threads (4 waves)
+  static constexpr int NT = 512;             // threads (8 waves, 2 per SIMD)
   static constexpr int ROWB = D * 2;         // bytes per K/V row
   static constexpr int SPR = ROWB / 16;      // 16-byte slots per row
   static constexpr int TILEB = BN * ROWB;    // bytes per K or V tile in LDS
   static constexpr int RPI = 1024 / ROWB;    // rows per 1 KB direct-to-LDS wave load
-  static constexpr int LPW = TILEB / 1024 / 4;  // such loads per wave per tile
+  static constexpr int LPW = TILEB / 1024 / 8;  // such loads per wave per tile
   static constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
   static constexpr int MB_O = D / 32;        // 32-row blocks of O^T
+  static constexpr int NA = 2 * KSTEPS;      // MFMAs of S^T per tile
+  static constexpr int NC = 4 * MB_O;        // MFMAs of O^T per tile
+  static_assert(NA == NC, "S and PV MFMA streams are interleaved one to one");
 };
 
 // LDS swizzles (16-byte slot index XOR a function of the row), chosen so the
@@ -71,19 +74,30 @@ constexpr float kRescaleThreshold = 8.0f;
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
+// Ping-pong schedule.  The two groups of 4 waves share the SIMDs pairwise and
+// run the same tile sequence half a step apart.  Per tile t a wave has a GEMM
+// phase G_t (S(t) = K(t) Q^T and O += P(t-1) V(t-1): MFMA only) and a softmax
+// phase X_t (mask, running max, exp, row sum of S(t): VALU only).  Group 0
+// runs G_t while group 1 runs X_{t-1}, then group 0 runs X_t while group 1
+// runs G_t, with a workgroup barrier between phases, so on every SIMD one
+// wave feeds the matrix cores while the other feeds the vector ALU.
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+__global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, float c, int nqb, int total) {
   using C = PrefillCfg<D>;
   using M = Mfma<BF16>;
   typedef typename M::op8 op8;
   typedef typename M::op2 op2;
-  constexpr int NA = 2 * C::KSTEPS;  // MFMAs of S^T per tile (2 key blocks x k-steps)
-  constexpr int NC = 4 * C::MB_O;    // MFMAs of O^T per tile (4 16-key steps x d blocks)
-  // two K and two V tile buffers: tile t+1's K and tile t's V are read while
-  // tile t+2's K and tile t+1's V arrive
-  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILEB];
+  // two K and two V tile buffers: K(t), V(t-1) are read in phases 2t, 2t+1;
+  // K(t+1) and V(t) arrive during them.  Four separate objects, each access
+  // naming its buffer statically, so the compiler can tell the tile loads in
+  // flight from the operand reads (one shared array would make every operand
+  // read wait for the loads issued just before it).
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
 
   const int logical = xcd_remap(blockIdx.x, total);
   const int bh = logical / nqb;
@@ -93,6 +107,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int off = Nk - Nq;        // bottom-right causal alignment
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
   const size_t qbase = (size_t)bh * Nq * D;
   const size_t kbase = (size_t)bh * Nk * D;
@@ -101,7 +116,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
 
   // B operand of S^T = K Q^T: lane holds Q[qrow][16kk + 8h .. +7]; rows past Nq read as 0
-  const int qrow = q0 + 32 * w + l32;
+  const int qmin_w = q0 + 128 * grp + 32 * wg;  // smallest query row of this wave
+  const int qrow = qmin_w + l32;
   op8 qop[C::KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < C::KSTEPS; ++kk)
@@ -112,14 +128,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
-  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+  const int T = (kv_end + C::BN - 1) / C::BN;
 
   // direct global -> LDS loads of one tile: wave w fills 1 KB blocks
   // LPW*w .. LPW*w + LPW-1; lane i lands at byte 16 i of its block (row i/SPR,
   // slot i%SPR) and therefore fetches global chunk slot ^ swizzle(row).
   // Keys past Nk read as 0 (buffer range check).
-  char* kb[2] = {smem, smem + C::TILEB};
-  char* vb[2] = {smem + 2 * C::TILEB, smem + 3 * C::TILEB};
   uint32_t gk_off[C::LPW], gv_off[C::LPW];
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
@@ -156,30 +170,75 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const s16x4 hi = lds_read_tr16(lv, a0 + 8 * C::ROWB);
     return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // S^T of one tile from the K tile in LDS (2 accumulators interleaved)
-  auto qk_tile = [&](const char* lk, f32x16* s) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-    op8 ka[2];
-    ka[0] = ka_load(lk, 0);
-    ka[1] = ka_load(lk, 1);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const op8 a = ka[i & 1];
-      if (i + 2 < NA) ka[i & 1] = ka_load(lk, i + 2);
-      s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
-    }
-  };
 
   f32x16 o[C::MB_O];
 #pragma unroll
   for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
+  f32x16 s[2];      // S(t) between its GEMM and softmax phases
+  op8 pb[4];        // P(t) between its softmax phase and the next GEMM phase
   float m_run = -INFINITY, l_run = 0.f;
-  const int qmin_w = q0 + 32 * w;  // smallest query row of this wave
 
-  // -inf on keys past Nk and (causal) on keys in a row's future; only tiles
-  // that hold such keys take this path
-  auto mask_tile = [&](int t, f32x16* s) {
+  // ---- G_t: S(t) (t < T) and O += P(t-1) V(t-1) (t >= 1), MFMA streams interleaved;
+  // lk holds K(t), lv holds V(t-1)
+  auto gemm_phase = [&](int t, const char* lk, const char* lv) {
+    const bool do_s = t < T, do_pv = t >= 1;
+    if (do_s && do_pv) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+      constexpr int PF = 4;  // operand reads in flight per stream
+      op8 ka[PF], va[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        ka[i] = ka_load(lk, i);
+        va[i] = va_load(lv, i);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NA; ++i) {
+        const op8 a = ka[i % PF], b = va[i % PF];
+        if (i + PF < C::NA) {
+          ka[i % PF] = ka_load(lk, i + PF);
+          va[i % PF] = va_load(lv, i + PF);
+        }
+        s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
+        o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
+      }
+      // issue order: the first PF steps' operand reads, then per step its two
+      // MFMAs each followed by the reads of the step PF ahead
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * PF, 0);
+#pragma unroll
+      for (int i = 0; i < C::NA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+    } else if (do_s) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+      op8 ka[2];
+      ka[0] = ka_load(lk, 0);
+      ka[1] = ka_load(lk, 1);
+#pragma unroll
+      for (int i = 0; i < C::NA; ++i) {
+        const op8 a = ka[i & 1];
+        if (i + 2 < C::NA) ka[i & 1] = ka_load(lk, i + 2);
+        s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
+      }
+    } else if (do_pv) {
+      op8 va[2];
+      va[0] = va_load(lv, 0);
+      va[1] = va_load(lv, 1);
+#pragma unroll
+      for (int i = 0; i < C::NC; ++i) {
+        const op8 b = va[i & 1];
+        if (i + 2 < C::NC) va[i & 1] = va_load(lv, i + 2);
+        o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
+      }
+    }
+  };
+
+  // ---- X_t: mask, running max, rescale, P(t) = exp2(S c - m), row sum
+  auto softmax_phase = [&](int t) {
     const int kv0 = t * C::BN;
     if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
       const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
@@ -191,12 +250,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
         }
     }
-  };
-  // running-max update for a tile: the max only moves when the tile's max
-  // exceeds it by more than the threshold (wave-uniform decision)
-  bool rescale;
-  float alpha;
-  auto tile_stats = [&](const f32x16* s, bool commit) {
     float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
     for (int i = 2; i < 16; ++i) {
@@ -204,40 +257,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       mx1 = fmaxf(mx1, s[1][i]);
     }
     const float mt = pair_max(fmaxf(mx0, mx1)) * c;
-    const bool r = __any(mt > m_run + kRescaleThreshold) && commit;
-    const float m_new = r ? fmaxf(m_run, mt) : m_run;
-    alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    rescale = r;
-    m_run = m_new;
-  };
-
-  // prologue: K(0), V(0), K(1) into LDS; S(0) and its statistics
-  load_tile(rk, gk_off, kb[0], 0);
-  load_tile(rv, gv_off, vb[0], 0);
-  if (ntiles > 1) load_tile(rk, gk_off, kb[1], 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 sa[2], sb[2];
-  qk_tile(kb[0], sa);
-  __syncthreads();  // every wave is done with K(0) before iteration 0 overwrites it
-  mask_tile(0, sa);
-  tile_stats(sa, true);
-
-  // one tile: the softmax of S(t) (statistics already known) overlaps the
-  // MFMAs of S(t+1); the MFMAs of O += P(t) V(t) overlap the row max of S(t+1)
-  auto step = [&](int t, f32x16* s_cur, f32x16* s_nxt) {
-    const bool has_next = t + 1 < ntiles;
-    if (t + 2 < ntiles) load_tile(rk, gk_off, kb[t & 1], t + 2);
-    if (has_next) load_tile(rv, gv_off, vb[(t + 1) & 1], t + 1);
-    if (rescale) {
+    float alpha = 1.f;
+    if (__any(mt > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mt);
+      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+      m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    // region A: S(t+1) on the MFMA (on the last tile this reads a stale buffer
-    // and the result is dropped), P(t) on the VALU
-    qk_tile(kb[(t + 1) & 1], s_nxt);
-    op8 pb[4];
     float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -245,8 +273,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       op2 pr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[nb][8 * tt + 2 * j], c, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[nb][8 * tt + 2 * j + 1], c, -m_use));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j], c, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use));
         pr[j] = M::pack2(p0, p1);
         lsum[j] += p0 + p1;
       }
@@ -254,35 +282,52 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
                                       __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
     }
     l_run = fmaf(l_run, alpha, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
-    // interleave: each MFMA of S(t+1) with its next operand read and a share of the softmax
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 120 / NA, 0);
-    }
-    // keep P(t) in region A (otherwise it is sunk next to its MFMA uses)
-    asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run));
-    if (has_next) mask_tile(t + 1, s_nxt);
-    // region B: O^T += V(t)^T P(t)^T on the MFMA, statistics of S(t+1) on the VALU
-    const char* lv = vb[t & 1];
-    op8 va[3];
-    va[0] = va_load(lv, 0);
-    va[1] = va_load(lv, 1);
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const op8 a = va[j % 3];
-      if (j + 2 < NC) va[(j + 2) % 3] = va_load(lv, j + 2);
-      o[j % C::MB_O] = M::mma(a, pb[j / C::MB_O], o[j % C::MB_O]);
-    }
-    tile_stats(s_nxt, has_next);
-    // the loads of K(t+2) and V(t+1) have landed in every wave's part of LDS
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < ntiles) step(t + 1, sb, sa);
+
+  // prologue: K(0) into LDS
+  load_tile(rk, gk_off, k0s, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // phase p: group 0 runs phase p of its own sequence G_0 X_0 G_1 X_1 ... G_T,
+  // group 1 runs phase p-1.  K(s+1) and V(s) are loaded during phases 2s and
+  // 2s+1 (into buffers last read in phases 2s-2 and 2s-1) and waited for at
+  // the end of phase 2s+1.  K(t) lives in buffer t%2, V(t) in buffer t%2, so
+  // the buffer roles repeat every 4 phases.
+  auto phase = [&](int p, const char* gk, const char* gv, char* ldk, char* ldv) {
+    if ((p & 1) == 0) {
+      const int st = p >> 1;
+      if (st + 1 < T) load_tile(rk, gk_off, ldk, st + 1);
+      if (st < T) load_tile(rv, gv_off, ldv, st);
+    }
+    const int mp = p - grp;
+    if (mp >= 0 && mp <= 2 * T) {
+      if ((mp & 1) == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        gemm_phase(mp >> 1, gk, gv);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        softmax_phase(mp >> 1);
+      }
+    }
+    if (p & 1) {
+      // the tile loads issued in phase p-1 have landed in every wave's part of LDS
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    } else {
+      // phase alignment only: nothing read in phase p+1 was written in phase p,
+      // so no fence (a fence would make this barrier wait for the loads just issued)
+      __builtin_amdgcn_s_barrier();
+    }
+  };
+  const int nphase = 2 * T + 2;  // even
+  for (int p = 0; p < nphase; p += 4) {
+    phase(p, k0s, v1s, k1s, v0s);      // G of even t: K(t) in k0, V(t-1) in v1; loads K(t+1)->k1, V(t)->v0
+    phase(p + 1, k0s, v1s, nullptr, nullptr);
+    if (p + 2 < nphase) {
+      phase(p + 2, k1s, v0s, k0s, v1s);  // G of odd t
+      phase(p + 3, k1s, v0s, nullptr, nullptr);
+    }
   }
 
   // ---- epilogue: combine the half-wave row sums, normalise, write O and LSE
