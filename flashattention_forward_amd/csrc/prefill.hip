@@ -51,12 +51,14 @@ struct PrefillCfg {
   static constexpr int SPR = ROWB / 16;      // 16-byte slots per row
   static constexpr int TILEB = BN * ROWB;    // bytes per K or V tile in LDS
   static constexpr int RPI = 1024 / ROWB;    // rows per 1 KB direct-to-LDS wave load
-  static constexpr int LPW = TILEB / 1024 / 8;  // such loads per wave per tile
+  static constexpr int LPG = TILEB / 1024 / 4;  // such loads per tile for each of the 4 loading waves
+  static constexpr int NLD = 2 * LPG;        // loads a wave issues per G phase (K tile, then V tile)
   static constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
   static constexpr int MB_O = D / 32;        // 32-row blocks of O^T
   static constexpr int NA = 2 * KSTEPS;      // MFMAs of S^T per tile
   static constexpr int NC = 4 * MB_O;        // MFMAs of O^T per tile
   static_assert(NA == NC, "S and PV MFMA streams are interleaved one to one");
+  static_assert(NA % NLD == 0, "loads are spread evenly over the MFMA steps");
 };
 
 // LDS swizzles (16-byte slot index XOR a function of the row), chosen so the
@@ -81,6 +83,13 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // runs G_t while group 1 runs X_{t-1}, then group 0 runs X_t while group 1
 // runs G_t, with a workgroup barrier between phases, so on every SIMD one
 // wave feeds the matrix cores while the other feeds the vector ALU.
+// one 1 KB direct global -> LDS load: lane i's 16 bytes at voff land at dst + 16 i
+// (a free function: the same builtin called from a lambda in the kernel made
+// the host compilation pass drop the kernel's launch stub)
+__device__ __forceinline__ void tile_load_lds(const __amdgpu_buffer_rsrc_t& r, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)dst, 16, voff, 0, 0, 0);
+}
+
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -130,24 +139,25 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
   const int T = (kv_end + C::BN - 1) / C::BN;
 
-  // direct global -> LDS loads of one tile: wave w fills 1 KB blocks
-  // LPW*w .. LPW*w + LPW-1; lane i lands at byte 16 i of its block (row i/SPR,
-  // slot i%SPR) and therefore fetches global chunk slot ^ swizzle(row).
-  // Keys past Nk read as 0 (buffer range check).
-  uint32_t gk_off[C::LPW], gv_off[C::LPW];
+  // direct global -> LDS loads of one tile, issued by the 4 waves of group 0
+  // only: wave wg fills 1 KB blocks LPG*wg .. LPG*wg + LPG-1; lane i lands at
+  // byte 16 i of its block (row i/SPR, slot i%SPR) and therefore fetches
+  // global chunk slot ^ swizzle(row).  Keys past Nk read as 0 (buffer range check).
+  uint32_t gk_off[C::LPG], gv_off[C::LPG];
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int blk = C::LPW * w + i;
+  for (int i = 0; i < C::LPG; ++i) {
+    const int blk = C::LPG * wg + i;
     const int row = blk * C::RPI + lane / C::SPR, slot = lane % C::SPR;
     gk_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ k_swz<D>(row));
     gv_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ v_swz<D>(row));
   }
-  auto load_tile = [&](const __amdgpu_buffer_rsrc_t& r, const uint32_t* goff, char* dst, int t) {
-    const uint32_t toff = (uint32_t)t * (C::BN * C::ROWB);
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)(dst + 1024 * (C::LPW * w + i)), 16,
-                                               toff + goff[i], 0, 0, 0);
+  // load q of the NLD a wave issues per G phase: K(tk) blocks first, then V(tv)
+  typedef __amdgpu_buffer_rsrc_t Rsrc;
+  auto issue_load = [&](const Rsrc& rk_, const Rsrc& rv_, int q, char* ldk, char* ldv, int tk, int tv) {
+    if (q < C::LPG)
+      tile_load_lds(rk_, ldk + 1024 * (C::LPG * wg + q), (uint32_t)tk * C::TILEB + gk_off[q]);
+    else
+      tile_load_lds(rv_, ldv + 1024 * (C::LPG * wg + q - C::LPG), (uint32_t)tv * C::TILEB + gv_off[q - C::LPG]);
   };
   // per-lane LDS operand offsets (constant across tiles)
   uint32_t ka_off[C::KSTEPS];  // K operand, row l32 (+32 per key block), logical slot 2kk+h
@@ -179,8 +189,13 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   // ---- G_t: S(t) (t < T) and O += P(t-1) V(t-1) (t >= 1), MFMA streams interleaved;
-  // lk holds K(t), lv holds V(t-1)
-  auto gemm_phase = [&](int t, const char* lk, const char* lv) {
+  // lk holds K(t), lv holds V(t-1).  With LD (group 0) it also issues the loads
+  // of K(t+1) into ldk and V(t) into ldv, one every STEP MFMA steps, so that the
+  // address unit sees a steady trickle rather than every wave's loads at once.
+  // K(t+1) is loaded even when t+1 = T: those rows read as 0 or are never used.
+  auto gemm_phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool LD, int t, const char* lk, const char* lv,
+                        char* ldk, char* ldv) {
+    constexpr int STEP = C::NA / C::NLD;
     const bool do_s = t < T, do_pv = t >= 1;
     if (do_s && do_pv) {
       s[0] = f32x16{};
@@ -201,9 +216,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         }
         s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
         o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
+        if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
       }
       // issue order: the first PF steps' operand reads, then per step its two
-      // MFMAs each followed by the reads of the step PF ahead
+      // MFMAs each followed by the reads of the step PF ahead, then its load
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * PF, 0);
 #pragma unroll
       for (int i = 0; i < C::NA; ++i) {
@@ -211,6 +227,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        if (LD && i % STEP == STEP - 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
       }
     } else if (do_s) {
       s[0] = f32x16{};
@@ -223,6 +240,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         const op8 a = ka[i & 1];
         if (i + 2 < C::NA) ka[i & 1] = ka_load(lk, i + 2);
         s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
+        if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
       }
     } else if (do_pv) {
       op8 va[2];
@@ -285,32 +303,31 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   };
 
   // prologue: K(0) into LDS
-  load_tile(rk, gk_off, k0s, 0);
+  if (grp == 0) {
+#pragma unroll
+    for (int q = 0; q < C::LPG; ++q) issue_load(rk, rv, q, k0s, nullptr, 0, 0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // phase p: group 0 runs phase p of its own sequence G_0 X_0 G_1 X_1 ... G_T,
-  // group 1 runs phase p-1.  K(s+1) and V(s) are loaded during phases 2s and
-  // 2s+1 (into buffers last read in phases 2s-2 and 2s-1) and waited for at
-  // the end of phase 2s+1.  K(t) lives in buffer t%2, V(t) in buffer t%2, so
-  // the buffer roles repeat every 4 phases.
-  auto phase = [&](int p, const char* gk, const char* gv, char* ldk, char* ldv) {
-    if ((p & 1) == 0) {
-      const int st = p >> 1;
-      if (st + 1 < T) load_tile(rk, gk_off, ldk, st + 1);
-      if (st < T) load_tile(rv, gv_off, ldv, st);
-    }
+  // group 1 runs phase p-1.  K(s+1) and V(s) are loaded by group 0 during its
+  // G_s in phase 2s (into buffers last read in phases 2s-2 and 2s-1) and
+  // waited for at the end of phase 2s+1.  K(t) lives in buffer t%2, V(t) in
+  // buffer t%2, so the buffer roles repeat every 4 phases.
+  auto phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool EVEN, int p, const char* gk, const char* gv, char* ldk,
+                   char* ldv) {
     const int mp = p - grp;
     if (mp >= 0 && mp <= 2 * T) {
       if ((mp & 1) == 0) {
         __builtin_amdgcn_s_setprio(1);
-        gemm_phase(mp >> 1, gk, gv);
+        gemm_phase(rk_, rv_, EVEN, mp >> 1, gk, gv, ldk, ldv);
         __builtin_amdgcn_s_setprio(0);
       } else {
         softmax_phase(mp >> 1);
       }
     }
-    if (p & 1) {
+    if (!EVEN) {
       // the tile loads issued in phase p-1 have landed in every wave's part of LDS
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -322,11 +339,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   };
   const int nphase = 2 * T + 2;  // even
   for (int p = 0; p < nphase; p += 4) {
-    phase(p, k0s, v1s, k1s, v0s);      // G of even t: K(t) in k0, V(t-1) in v1; loads K(t+1)->k1, V(t)->v0
-    phase(p + 1, k0s, v1s, nullptr, nullptr);
+    phase(rk, rv, true, p, k0s, v1s, k1s, v0s);  // G of even t: K(t) in k0, V(t-1) in v1; loads K(t+1)->k1, V(t)->v0
+    phase(rk, rv, false, p + 1, k0s, v1s, k1s, v0s);
     if (p + 2 < nphase) {
-      phase(p + 2, k1s, v0s, k0s, v1s);  // G of odd t
-      phase(p + 3, k1s, v0s, nullptr, nullptr);
+      phase(rk, rv, true, p + 2, k1s, v0s, k0s, v1s);  // G of odd t
+      phase(rk, rv, false, p + 3, k1s, v0s, k0s, v1s);
     }
   }
 
