@@ -19,6 +19,16 @@ Printed as ONE JSON line, which also carries
     way (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                       [--copy-calibration]
+       python bench.py --traffic-from FETCH_DIR WRITE_DIR
+
+HBM traffic: two rocprofv3 counter runs of
+    python bench.py --no-cpu-baseline --no-extra --steps 3 --warmup 1 --copy-calibration
+one with --pmc FETCH_SIZE and one with --pmc WRITE_SIZE (CSV output).  The
+--copy-calibration flag adds, before the timed region, three plain device
+copies of COPY_BYTES bytes (torch's copy kernel reads and writes exactly that
+many bytes), so each counter is scaled by known bytes / what it reads for
+the copy.  --traffic-from turns the two runs into profiles/prefill_4k_traffic.json.
 """
 from __future__ import annotations
 
@@ -37,14 +47,22 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # dense fp8 / int8
 PEAK_HBM_GBS = 8000.0         # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4k_traffic.json")
+COPY_BYTES = 1 << 30          # bytes read (and written) by one calibration copy
+PREFILL_KERNEL = "prefill_kernel<128, true, false>"   # bf16, non-causal
 KERNEL_SOURCES = ["flashattention_forward_amd/csrc/prefill.hip", "flashattention_forward_amd/csrc/common.h"]
 
 
 def kernel_source_sha() -> str:
+    """Hash of the prefill kernel's code with comments and blank space removed,
+    so that the counter record goes stale when the code changes, not its prose."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(" ".join(l.split()) for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -58,6 +76,58 @@ def traffic_per_launch():
     if rec.get("kernel_source_sha") != kernel_source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(run_dir: str, counter: str):
+    """(kernel name, value) per dispatch of `counter` from a rocprofv3 CSV run."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {run_dir}")
+    return rows
+
+
+def traffic_from(fetch_dir: str, write_dir: str) -> dict:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the non-causal prefill
+    kernel by the copy calibration and write the traffic record."""
+    out = {"kernel": PREFILL_KERNEL, "kernel_source_sha": kernel_source_sha(), "copy_bytes": COPY_BYTES}
+    total = 0.0
+    for name, run_dir, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(run_dir, counter)
+        copy = [v for k, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
+        pre = [v for k, v in rows if PREFILL_KERNEL in k]
+        if not copy or not pre:
+            raise SystemExit(f"{counter}: need both copy and {PREFILL_KERNEL} dispatches under {run_dir}")
+        copy_kib = sorted(copy)[len(copy) // 2]
+        pre_kib = sum(pre) / len(pre)
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        out[name] = {"counter": counter, "prefill_kib_per_dispatch": round(pre_kib, 1),
+                     "copy_kib_per_dispatch": round(copy_kib, 1), "bytes_per_counter_byte": round(factor, 4),
+                     "prefill_bytes_per_launch": round(pre_kib * 1024.0 * factor)}
+        total += pre_kib * 1024.0 * factor
+    out["hbm_bytes_per_launch"] = round(total)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
+def copy_calibration():
+    """Three plain device copies of COPY_BYTES bytes (untimed)."""
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def timed_launches(fns, steps, warmup):
@@ -86,7 +156,7 @@ def timed_launches(fns, steps, warmup):
     return total, per
 
 
-def cpu_baseline(seconds_target: float = 15.0):
+def cpu_baseline(seconds_target: float = 15.0, max_heads: int = 1024):
     """The fp64 oracle on a bounded sample of the prefill workload: whole
     heads, alternating non-causal and causal, until ~seconds_target."""
     import numpy as np
@@ -101,7 +171,7 @@ def cpu_baseline(seconds_target: float = 15.0):
     flops = 0.0
     heads = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds_target and heads < 64:
+    while time.perf_counter() - t0 < seconds_target and heads < max_heads:
         b, h = divmod(heads, w.H)
         q, k, v = (G.to_f64(x[0], "bf16") for x in G.draw_qkv(w, heads=[(b, h)]))
         causal = bool(heads % 2)
@@ -121,10 +191,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from(*args.traffic_from)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (attention shards by (batch, head) "
-              "with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (the forward pass shards by "
+              "(batch, head) with no exchange between GPUs, so one GPU's share is the measured unit). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -134,6 +210,8 @@ def main():
 
     F.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
     w = G.WORKLOADS["prefill_4k"]
     q, k, v = (G.to_torch(x, "bf16") for x in G.draw_qkv(w, threads=16))
     out_nc, out_c = torch.empty_like(q), torch.empty_like(q)

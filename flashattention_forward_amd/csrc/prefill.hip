@@ -12,11 +12,11 @@
 // deferred to the end.  Causal blocks stop at the diagonal ("Causal
 // masking": tiles holding only future keys are never loaded).
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 query rows, key tiles of 64):
+// gfx950 mapping (one workgroup = 8 waves = 256 query rows, key tiles of 64):
 //   * S^T = K Q^T on 32x32x16 MFMA: the K tile (LDS) is the A operand and the
 //     wave's Q rows (VGPRs, loaded once) the B operand.  Working on S^T puts
 //     one query per lane (16 keys in each of lanes l and l^32), so the row
-//     max is 31 in-lane max ops and one exchange between the two half-waves.
+//     max is in-lane max ops and one exchange between the two half-waves.
 //   * O^T += V^T P^T on 32x32x16 MFMA: P^T is the S^T accumulator converted
 //     in registers (no LDS round trip: the accumulator layout of S^T is the
 //     B-operand layout once the keys of each 16-key step are taken in the
@@ -26,14 +26,22 @@
 //     and one v_exp_f32 per score; the row sum l adds the fp32 P (rounding P
 //     to bf16 first would cost up to 2^-8 of l on rows with few keys).
 //   * The running max is only raised when a tile's max exceeds it by more
-//     than 2^8 (the adaptive rescaling of "Smarter online softmax rescaling"
-//     in the linux-konsole.com post "FlashAttention 4: fast, memory-efficient
-//     attention for LLMs"): P then stays below 2^8, and O and l are rescaled
-//     only on those rare tiles.  The result is exact after the final 1/l.
-//   * K/V tiles are staged through registers: the global loads of tile t+1
-//     are issued before the MFMAs of tile t and written to LDS after it.
-//   * LDS rows are padded (K: +16 B, V: +64 B per row) so the 16-byte K reads
-//     and the transposing V reads of one wave fall on distinct banks.
+//     than 8 in log2 units (the adaptive rescaling of "Smarter online softmax
+//     rescaling" in the linux-konsole.com post "FlashAttention 4: fast,
+//     memory-efficient attention for LLMs"): P then stays below 2^8, and O
+//     and l are rescaled only on those rare tiles.  The result is exact
+//     after the final 1/l.
+//   * Two groups of 4 waves alternate: while one group runs the MFMAs of its
+//     tile (S(t) and O += P(t-1) V(t-1), the two streams interleaved), the
+//     other runs the softmax of its previous tile, so the matrix cores and
+//     the vector ALUs of a SIMD (which holds one wave of each group) work at
+//     the same time; a workgroup barrier ends every phase.
+//   * K/V tiles go from global memory straight into LDS (buffer loads with
+//     the LDS-destination form, 1 KB per wave instruction), double-buffered;
+//     only the waves in their MFMA phase issue them, one every other MFMA
+//     step, and the buffer range check turns keys past Nk into zeros.  The
+//     16-byte slots of each LDS row are XOR-swizzled on the load side so the
+//     K operand reads and the transposing V reads hit distinct banks.
 //   * Workgroups are renumbered so each XCD walks a contiguous range of
 //     (head, query block) items (K/V of a head stay in that XCD's L2);
 //     causal grids start with the longest (bottom) query blocks.
