@@ -176,6 +176,29 @@ def test_full_size_sampled(F, name):
     assert worst_o <= O_TOL and worst_l <= LSE_TOL
 
 
+@pytest.mark.parametrize("Nq,Nk,d,dtype", [(600, 600, 64, "bf16"), (520, 700, 128, "fp16"), (900, 900, 128, "bf16"),
+                                         (1100, 1100, 64, "fp16")])
+def test_causal_many_heads(F, Nq, Nk, d, dtype):
+    """Causal grids with enough (batch, head) pairs that the launcher puts two
+    query blocks (the longest and the shortest left) in one workgroup: odd
+    and even block counts, a ragged last block, Nq < Nk.  Whole heads of a
+    sample are compared with the oracle."""
+    w = G.Workload("causal_many_heads", 60, 4, 128, Nq, Nk, d, dtype, 1.0, True, d ** -0.5)
+    q, k, v = G.draw_qkv(w, threads=16)
+    out, lse = _run(F, q, k, v, w, True)
+    from tests.gpu_util import from_dev
+    o_all, l_all = from_dev(out), from_dev(lse)
+    assert np.isfinite(o_all).all() and np.isfinite(l_all).all()
+    worst_o = worst_l = 0.0
+    for (b, h) in _sampled_heads(w, 4):
+        f = lambda x: G.to_f64(x[b, h], w.dtype)
+        O, L = A.attention_head(f(q), f(k), f(v), w.scale, True)
+        worst_o = max(worst_o, np.abs(o_all[b, h] - O).max())
+        worst_l = max(worst_l, np.abs(l_all[b, h] - L).max())
+    print(f"  sampled heads max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}", flush=True)
+    assert worst_o <= O_TOL and worst_l <= LSE_TOL
+
+
 def test_long_sequence_memory(F):
     """One trading day (N = 23400, 12 heads, fp16): the naive N x N fp16 score
     matrix would take 13.1 GB; the tiled forward allocates nothing beyond its
