@@ -55,7 +55,9 @@ namespace attn {
 template <int D>
 struct PrefillCfg {
   static constexpr int BM = 256;             // query rows per workgroup: 2 groups x 4 waves x 32
-  static constexpr int BN = 64;              // keys per tile
+  static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile (multiple of 32)
+  static constexpr int NB = BN / 32;         // 32-key blocks of S^T per tile
+  static constexpr int NG = BN / 16;         // 16-key groups (k-steps of O^T) per tile
   static constexpr int NT = 512;             // threads (8 waves, 2 per SIMD)
   static constexpr int ROWB = D * 2;         // bytes per K/V row
   static constexpr int SPR = ROWB / 16;      // 16-byte slots per row
@@ -65,8 +67,8 @@ struct PrefillCfg {
   static constexpr int NLD = 2 * LPG;        // loads a wave issues per G phase (K tile, then V tile)
   static constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
   static constexpr int MB_O = D / 32;        // 32-row blocks of O^T
-  static constexpr int NA = 2 * KSTEPS;      // MFMAs of S^T per tile
-  static constexpr int NC = 4 * MB_O;        // MFMAs of O^T per tile
+  static constexpr int NA = NB * KSTEPS;     // MFMAs of S^T per tile
+  static constexpr int NC = NG * MB_O;       // MFMAs of O^T per tile
   static_assert(NA == NC, "S and PV MFMA streams are interleaved one to one");
   static_assert(NA % NLD == 0, "loads are spread evenly over the MFMA steps");
 };
@@ -170,8 +172,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
     va_off[mb] = vrow * C::ROWB + 16 * ((col >> 3) ^ v_swz<D>(vrow)) + 2 * (col & 7);
   }
-  auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i&1, k-step i>>1
-    return lds_load<op8>(lk, ka_off[i >> 1] + (i & 1) * 32 * C::ROWB);
+  auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i%NB, k-step i/NB
+    return lds_load<op8>(lk, ka_off[i / C::NB] + (i % C::NB) * 32 * C::ROWB);
   };
   auto va_load = [&](const char* lv, int j) {  // V^T operand of O^T step j: 16-key group j/MB_O, d block j%MB_O
     const uint32_t a0 = va_off[j % C::MB_O] + 16 * (j / C::MB_O) * C::ROWB;
@@ -201,8 +203,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     f32x16 o[C::MB_O];
 #pragma unroll
     for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
-    f32x16 s[2];      // S(t) between its GEMM and softmax phases
-    op8 pb[4];        // P(t) between its softmax phase and the next GEMM phase
+    f32x16 s[C::NB];  // S(t) between its GEMM and softmax phases
+    op8 pb[C::NG];    // P(t) between its softmax phase and the next GEMM phase
     float m_run = -INFINITY, l_run = 0.f;
 
     // ---- G_t: S(t) (t < T) and O += P(t-1) V(t-1) (t >= 1), MFMA streams interleaved;
@@ -215,8 +217,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       constexpr int STEP = C::NA / C::NLD;
       const bool do_s = t < T, do_pv = t >= 1;
       if (do_s && do_pv) {
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
         constexpr int PF = 4;  // operand reads in flight per stream
         op8 ka[PF], va[PF];
 #pragma unroll
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             ka[i % PF] = ka_load(lk, i + PF);
             va[i % PF] = va_load(lv, i + PF);
           }
-          s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
+          s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
           o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
           if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
         }
@@ -247,8 +249,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
           if (LD && i % STEP == STEP - 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
         }
       } else if (do_s) {
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
         op8 ka[2];
         ka[0] = ka_load(lk, 0);
         ka[1] = ka_load(lk, 1);
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         for (int i = 0; i < C::NA; ++i) {
           const op8 a = ka[i & 1];
           if (i + 2 < C::NA) ka[i & 1] = ka_load(lk, i + 2);
-          s[i & 1] = M::mma(a, qop[i >> 1], s[i & 1]);
+          s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
           if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
         }
       } else if (do_pv) {
@@ -278,20 +280,23 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
         const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
             if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
           }
       }
-      float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
+      float mx[C::NB];
 #pragma unroll
-      for (int i = 2; i < 16; ++i) {
-        mx0 = fmaxf(mx0, s[0][i]);
-        mx1 = fmaxf(mx1, s[1][i]);
+      for (int nb = 0; nb < C::NB; ++nb) {
+        mx[nb] = fmaxf(s[nb][0], s[nb][1]);
+#pragma unroll
+        for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
       }
-      const float mt = pair_max(fmaxf(mx0, mx1)) * c;
+#pragma unroll
+      for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
+      const float mt = pair_max(mx[0]) * c;
       float alpha = 1.f;
       if (__any(mt > m_run + kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, mt);
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < C::NG; ++g) {
         const int nb = g >> 1, tt = g & 1;
         op2 pr[4];
 #pragma unroll
