@@ -20,6 +20,8 @@
 //     applies v_scale / l.
 // The quantisation kernels (per-token int8, per-tensor E4M3) and two test
 // hooks that run this file's own tile routines live here as well.
+#include <cfloat>
+
 #include "common.h"
 #include "internal.h"
 
@@ -273,7 +275,10 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
   const int qrow = q0 + 32 * w + l32;
   i32x4 qop[C::KSTEPS];
   load_q8_operand(Q8 + (qbase + qrow) * C::D, qrow < Nq, h, qop);
-  const float cq = (qrow < Nq ? QS[qbase + qrow] : 0.f) * c;
+  // query scale x softmax scale x log2 e, applied in the exponent's FMA; kept
+  // positive (a zero query row has zero scores, so its scale is immaterial) so
+  // that masked -inf scores stay -inf
+  const float cq = fmaxf((qrow < Nq ? QS[qbase + qrow] : 0.f) * c, FLT_MIN);
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
         for (int g = 0; g < 4; ++g) {
           const f32x4 ks4 = lds_load<f32x4>(reinterpret_cast<const char*>(lks), (32 * nb + 8 * g + 4 * h) * 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[nb][4 * g + j] = (float)acc[nb][4 * g + j] * ks4[j] * cq;
+          for (int j = 0; j < 4; ++j) s[nb][4 * g + j] = (float)acc[nb][4 * g + j] * ks4[j];
         }
       const bool need_mask = (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
       if (need_mask) {
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
-      mt = pair_max(mt);
+      mt = pair_max(mt) * cq;
       if (__any(mt > m_run + kRescaleThresholdQ)) {
         const float mn = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
@@ -336,10 +341,10 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
 #pragma unroll
       for (int jw = 0; jw < 8; ++jw) {
         const int nb = jw >> 2, i0 = 4 * (jw & 3);
-        const float p0 = __builtin_amdgcn_exp2f(s[nb][i0 + 0] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(s[nb][i0 + 1] - m_use);
-        const float p2 = __builtin_amdgcn_exp2f(s[nb][i0 + 2] - m_use);
-        const float p3 = __builtin_amdgcn_exp2f(s[nb][i0 + 3] - m_use);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 0], cq, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 1], cq, -m_use));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 2], cq, -m_use));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 3], cq, -m_use));
         l_run += (p0 + p1) + (p2 + p3);
         pb[jw] = (int)e4m3x4(p0, p1, p2, p3);
       }
