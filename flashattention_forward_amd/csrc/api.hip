@@ -15,10 +15,16 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 
-// grid of the prefill kernels: ceil(Nq / 128) * B * H workgroups, must fit an int
+// the prefill grid has at most ceil(Nq / 128) * B * H workgroups; it must fit an int
 bool prefill_grid_ok(int B, int H, int Nq) {
   const long long g = ((long long)Nq + 127) / 128 * (long long)B * (long long)H;
   return g <= INT_MAX;
+}
+
+// the bf16/fp16 prefill addresses one head through buffer descriptors with
+// 32-bit sizes and offsets
+bool prefill_head_ok(int Nq, int Nk, int d) {
+  return (long long)Nq * d * 2 <= (long long)UINT32_MAX && (long long)Nk * d * 2 <= (long long)UINT32_MAX;
 }
 
 int check_common(const void* q, const void* k, const void* v, const void* out, const float* lse, int B, int H, int Nq,
@@ -80,6 +86,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     const int splits = attn::decode_default_splits(B, H, Nk, d);
     return attn_fwd_decode(q, k, v, out, lse, B, H, Nk, d, scale, dtype, splits, workspace, workspace_bytes, stream);
   }
+  if (!prefill_head_ok(Nq, Nk, d)) return ATTN_E_INVALID;
   return hip_status(attn::launch_prefill(q, k, v, out, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype == ATTN_BF16,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -136,7 +143,7 @@ int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream) {
 const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
-    case ATTN_E_INVALID: return "invalid argument (null/misaligned pointer, bad size or scale, causal with Nq > Nk)";
+    case ATTN_E_INVALID: return "invalid argument (null/misaligned pointer, bad or too large size, bad scale, causal with Nq > Nk)";
     case ATTN_E_UNSUPPORTED: return "unsupported head size or dtype";
     case ATTN_E_WORKSPACE: return "workspace missing or too small";
     case ATTN_E_HIP: return "HIP launch error";

@@ -51,7 +51,8 @@ extern "C" {
 /* Return codes. */
 enum {
   ATTN_OK = 0,
-  ATTN_E_INVALID = -1,     /* null/misaligned pointer, non-positive size, bad scale, causal with Nq > Nk */
+  ATTN_E_INVALID = -1,     /* null/misaligned pointer, non-positive or too large size, bad scale,
+                              causal with Nq > Nk */
   ATTN_E_UNSUPPORTED = -2, /* head size or dtype outside what is built */
   ATTN_E_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes() */
   ATTN_E_HIP = -4          /* a HIP launch error was reported */
@@ -81,7 +82,8 @@ size_t attn_fwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
  *   after the call are unspecified.
  * Nq == 1 dispatches to the split-KV decode kernels (partials over key
  * ranges, then a log-sum-exp merge); every other Nq runs the tiled prefill
- * kernel.
+ * kernel, which addresses one head of Q, K or V in 32 bits: Nq*d*2 and
+ * Nk*d*2 must stay below 2^32 bytes (ATTN_E_INVALID otherwise).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,

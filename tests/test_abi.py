@@ -52,6 +52,8 @@ def fwd(**kw):
     (dict(scale=float("nan")), Bd.ATTN_E_INVALID), (dict(scale=float("inf")), Bd.ATTN_E_INVALID),
     (dict(causal=1, Nq=5, Nk=4), Bd.ATTN_E_INVALID),
     (dict(B=2 ** 20, H=2 ** 20), Bd.ATTN_E_INVALID),
+    # one head of K past 2^32 bytes (the prefill's 32-bit buffer descriptors)
+    (dict(Nk=2 ** 24, d=128), Bd.ATTN_E_INVALID), (dict(Nq=2 ** 25, Nk=2 ** 25, d=64), Bd.ATTN_E_INVALID),
     (dict(d=96), Bd.ATTN_E_UNSUPPORTED), (dict(d=256), Bd.ATTN_E_UNSUPPORTED), (dict(dtype=2), Bd.ATTN_E_UNSUPPORTED),
     (dict(Nq=1, ws=None, wsb=0), Bd.ATTN_E_WORKSPACE), (dict(Nq=1, ws=A, wsb=16), Bd.ATTN_E_WORKSPACE),
     (dict(Nq=1, ws=MIS, wsb=1 << 20), Bd.ATTN_E_WORKSPACE),
