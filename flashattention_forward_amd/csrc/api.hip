@@ -152,10 +152,11 @@ const char* attn_status_str(int status) {
 }
 
 const char* attn_build_info(void) {
-  return "libattn_mi355x: gfx950; prefill bf16/fp16 d={64,128} BM=128 BN=64 4 waves (32 rows/wave), "
-         "32x32x16 MFMA, S^T=KQ^T, V^T via ds_read_b64_tr_b16, rescale threshold 2^8; "
+  return "libattn_mi355x: gfx950; prefill bf16/fp16 d={64,128} BM=256 (8 waves, 2 groups ping-ponging MFMA and "
+         "softmax phases, 32 rows/wave), BN=64 (d=128) / 128 (d=64), direct-to-LDS K/V tiles, 32x32x16 MFMA, "
+         "S^T=KQ^T, V^T via ds_read_b64_tr_b16, rescale threshold 2^8, causal blocks paired on large grids; "
          "decode split-KV 256 threads, 8 rows in flight/lane + LSE merge; "
-         "q8 prefill d=128 int8 32x32x32 + fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8";
+         "q8 prefill d=128 BM=128 BN=64, int8 32x32x32 + fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8";
 }
 
 }  // extern "C"
