@@ -30,7 +30,9 @@ Modules:
                  partial states over disjoint key ranges.
   quant       -- int8 per-token and OCP e4m3 quantisation emulation and the
                  quantised-attention oracle.
+  backward    -- the gradients dQ, dK, dV of attention by the chain rule
+                 through the plain definition.
 
 Parity status of every function is stated in its module header.
 """
-from . import attention, quant, recurrence  # noqa: F401
+from . import attention, backward, quant, recurrence  # noqa: F401

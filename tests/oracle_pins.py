@@ -305,3 +305,117 @@ def pin_q8_attention(attn_q8, decode, tol=1e-13):
     p1 = math.exp(float(sk[1]) - 1.0)
     assert abs(O[0, 0] - (1.0 + 0.3125 * 2.0) / (1.0 + p1)) <= 1e-12
     assert abs(L[0] - (1.0 + math.log1p(p1))) <= 1e-12
+
+
+# ---------------------------------------------------------------- backward
+#
+# ``bwd(q, k, v, do, scale, causal) -> (dQ, dK, dV)`` works on one head, fp64.
+
+_BWD_SHAPES = [(3, 5, 2, 3, False), (4, 4, 3, 2, True), (2, 6, 4, 4, True), (5, 5, 2, 2, False)]
+
+
+def pin_bwd_finite_difference(bwd, fwd, h=1e-5, tol=2e-8):
+    """Central differences of L = sum(dO * O) through the forward definition
+    (itself pinned above), one input entry at a time: the gradient is what the
+    forward's derivative is, whatever formula produced it."""
+    for (Nq, Nk, d, dv, causal) in _BWD_SHAPES:
+        q, k, v, do = _rand(Nq, d), _rand(Nk, d), _rand(Nk, dv), _rand(Nq, dv)
+        scale = 0.6
+        got = bwd(q, k, v, do, scale, causal)
+        for which, x in enumerate((q, k, v)):
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which] = xp
+                args_m[which] = xm
+                lp = float(np.sum(do * fwd(*args_p, scale, causal)[0]))
+                lm = float(np.sum(do * fwd(*args_m, scale, causal)[0]))
+                fd = (lp - lm) / (2 * h)
+                assert abs(fd - got[which][idx]) <= tol * max(1.0, abs(fd)), (which, idx, fd, got[which][idx])
+
+
+def pin_bwd_torch(bwd, tol=1e-12):
+    """torch's CPU float64 autograd (library) of softmax(scale Q K^T + mask) V,
+    with the bottom-right causal mask built explicitly."""
+    for (Nq, Nk, d, causal) in [(7, 7, 8, False), (7, 7, 8, True), (5, 13, 4, True), (9, 4, 6, False)]:
+        q, k, v, do = _rand(Nq, d), _rand(Nk, d), _rand(Nk, d), _rand(Nq, d)
+        scale = 1.0 / math.sqrt(d)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        s = (tq @ tk.T) * scale
+        if causal:
+            vis = torch.arange(Nk)[None, :] <= torch.arange(Nq)[:, None] + (Nk - Nq)
+            s = s.masked_fill(~vis, float("-inf"))
+        o = torch.softmax(s, dim=-1) @ tv
+        o.backward(torch.tensor(do))
+        got = bwd(q, k, v, do, scale, causal)
+        for g, t in zip(got, (tq, tk, tv)):
+            assert np.max(np.abs(g - t.grad.numpy())) <= tol
+
+
+def pin_bwd_uniform(bwd, tol=1e-13):
+    """Q = 0 makes every visible score 0 (closed form): P is uniform over the
+    visible keys, so dV_j = sum over the queries that see key j of dO_i / n_i,
+    dK = 0, and dQ_i = scale * C_i^T dO_i with C_i the covariance
+    (1/n_i) sum_j (v_j - vbar_i)(k_j - kbar_i)^T over row i's n_i keys."""
+    for (Nq, Nk, d, dv, causal) in [(4, 7, 3, 2, False), (5, 5, 2, 3, True), (3, 8, 4, 4, True)]:
+        k, v, do = _rand(Nk, d), _rand(Nk, dv), _rand(Nq, dv)
+        scale = 0.8
+        dq, dk, dvv = bwd(np.zeros((Nq, d)), k, v, do, scale, causal)
+        want_dv = np.zeros((Nk, dv))
+        for i in range(Nq):
+            n = (i + Nk - Nq + 1) if causal else Nk
+            want_dv[:n] += do[i] / n
+            kc, vc = k[:n] - k[:n].mean(axis=0), v[:n] - v[:n].mean(axis=0)
+            cov = vc.T @ kc / n                      # [dv, d]
+            assert np.max(np.abs(dq[i] - scale * (cov.T @ do[i]))) <= tol
+        assert np.max(np.abs(dvv - want_dv)) <= tol and np.max(np.abs(dk)) <= tol
+
+
+def pin_bwd_sums(bwd, tol=1e-12):
+    """Invariants of the definition: every row of dS sums to zero, so the
+    rows of dK sum to zero; every row of P sums to one, so the rows of dV sum
+    to the rows of dO; dO = 0 gives zero gradients; the gradient is linear in
+    dO."""
+    for (Nq, Nk, d, dv, causal) in _BWD_SHAPES:
+        q, k, v, do = _rand(Nq, d), _rand(Nk, d), _rand(Nk, dv), _rand(Nq, dv)
+        dq, dk, dvv = bwd(q, k, v, do, 0.7, causal)
+        assert np.max(np.abs(dk.sum(axis=0))) <= tol
+        assert np.max(np.abs(dvv.sum(axis=0) - do.sum(axis=0))) <= tol
+        for g in bwd(q, k, v, np.zeros_like(do), 0.7, causal):
+            assert np.max(np.abs(g)) == 0.0
+        g2 = bwd(q, k, v, -2.5 * do, 0.7, causal)
+        for a, b in zip((dq, dk, dvv), g2):
+            assert np.max(np.abs(-2.5 * a - b)) <= tol
+
+
+def pin_bwd_key_shift(bwd, tol=1e-12):
+    """K -> K + 1 u^T adds scale * q_i . u to every visible score of row i,
+    which leaves P (and so dV and dS) unchanged; since the rows of dS sum to
+    zero, dQ = scale dS K is unchanged too, and dK is unchanged outright."""
+    for (Nq, Nk, d, dv, causal) in _BWD_SHAPES:
+        q, k, v, do = _rand(Nq, d), _rand(Nk, d), _rand(Nk, dv), _rand(Nq, dv)
+        u = _rand(d)
+        a = bwd(q, k, v, do, 0.5, causal)
+        b = bwd(q, k + u[None, :], v, do, 0.5, causal)
+        for x, y in zip(a, b):
+            assert np.max(np.abs(x - y)) <= tol
+
+
+def pin_bwd_causal_first_row(bwd, tol=1e-12):
+    """Causal with Nq = Nk: query 0 sees only key 0, so P_00 = 1, dS_0j = 0
+    and dQ_0 = 0, while key Nk-1 is seen only by the last query: its dV row
+    is that query's dO times P_{N-1,N-1}."""
+    N, d = 6, 3
+    q, k, v, do = _rand(N, d), _rand(N, d), _rand(N, d), _rand(N, d)
+    dq, dk, dvv = bwd(q, k, v, do, 0.9, True)
+    assert np.max(np.abs(dq[0])) <= tol
+    s = (q[-1] @ k.T) * 0.9
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    assert np.max(np.abs(dvv[-1] - p[-1] * do[-1])) <= tol
+
+
+BACKWARD_PINS = [pin_bwd_torch, pin_bwd_uniform, pin_bwd_sums, pin_bwd_key_shift, pin_bwd_causal_first_row]

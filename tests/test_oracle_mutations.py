@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import attention as A
+from oracle import backward as BW
 from oracle import quant as Q
 from oracle import recurrence as R
 from tests import oracle_pins as P
@@ -231,3 +232,57 @@ def test_unmutated_q8_copy_equals_oracle():
 def test_q8_attention_mistake_is_caught(mistake):
     with pytest.raises(AssertionError):
         P.pin_q8_attention(lambda *a: q8_attention_variant(*a, mistake=mistake), Q.e4m3_decode)
+
+
+def bwd_variant(q, k, v, do, scale, causal, mistake=None):
+    """The chain rule of oracle.backward with one switchable mistake."""
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    Nq, Nk = q.shape[0], k.shape[0]
+    s = q @ k.T * scale
+    if causal:
+        i = np.arange(Nq)[:, None]
+        j = np.arange(Nk)[None, :]
+        vis = {"causal_strict": j < i + (Nk - Nq), "causal_top_left": j <= i}.get(mistake, j <= i + (Nk - Nq))
+        if mistake != "no_mask":
+            s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    p = e / e.sum(axis=1)[:, None]
+    dv = (e if mistake == "dv_unnormalised" else p).T @ do
+    dp = do @ v.T
+    if mistake == "drop_softmax_term":
+        ds = p * dp
+    elif mistake == "softmax_term_over_columns":
+        ds = p * (dp - (p * dp).sum(axis=0)[None, :])
+    elif mistake == "softmax_term_sign":
+        ds = p * ((p * dp).sum(axis=1)[:, None] - dp)
+    else:
+        ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+    dq = (1.0 if mistake == "dq_no_scale" else scale) * (ds @ (v if mistake == "dq_uses_v" else k))
+    dk = (1.0 if mistake == "dk_no_scale" else scale) * ((ds if mistake == "dk_untransposed_ds" else ds.T) @ q)
+    return dq, dk, dv
+
+
+BWD_MISTAKES = ["causal_strict", "causal_top_left", "no_mask", "dv_unnormalised", "drop_softmax_term",
+                "softmax_term_over_columns", "softmax_term_sign", "dq_no_scale", "dq_uses_v", "dk_no_scale",
+                "dk_untransposed_ds"]
+
+
+def test_unmutated_backward_copy_equals_oracle():
+    rng = np.random.default_rng(9)
+    for causal in (False, True):
+        q, k, v, do = (rng.standard_normal((5, 4)), rng.standard_normal((9, 4)), rng.standard_normal((9, 3)),
+                       rng.standard_normal((5, 3)))
+        for a, b in zip(bwd_variant(q, k, v, do, 0.5, causal), BW.attention_backward_head(q, k, v, do, 0.5, causal)):
+            assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("mistake", BWD_MISTAKES)
+def test_backward_mistake_is_caught(mistake):
+    fwd = lambda q, k, v, s, c: A.attention_head(q, k, v, s, c)
+    fd = lambda fn: P.pin_bwd_finite_difference(fn, fwd)
+    fd.__name__ = "pin_bwd_finite_difference"
+    with np.errstate(all="ignore"):
+        failed = _fails_some_pin(lambda q, k, v, do, s, c: bwd_variant(q, k, v, do, s, c, mistake),
+                                 P.BACKWARD_PINS + [fd])
+    assert failed, f"no pin catches {mistake}"
