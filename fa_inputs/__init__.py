@@ -8,7 +8,9 @@ quantisation of the method).
 Recipe (every tensor of every workload):
   * one numpy PCG64 stream per (workload id, tensor id, batch, head):
     ``np.random.default_rng([seed, workload_id, tensor_id, b, h])`` with
-    tensor ids Q=0, K=1, V=2, so any single head can be regenerated alone;
+    tensor ids Q=0, K=1, V=2 and, for the backward pass, the upstream
+    gradient dO=3 (shaped like Q), so any single head can be regenerated
+    alone;
   * ``standard_normal(dtype=float32)`` of shape [N, d], times sigma in fp32;
   * one round-to-nearest-even to the storage type (bf16 via the bit pattern,
     fp16 via numpy's IEEE conversion) -- no double rounding through fp64.
@@ -23,7 +25,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TENSOR_ID = {"q": 0, "k": 1, "v": 2}
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -113,7 +115,7 @@ def draw_tensor(w: Workload, tensor: str, seed: int = 0, heads=None,
                 threads: int = 8) -> np.ndarray:
     """A whole tensor [B, H, N, d] (or the listed (b, h) heads stacked as
     [len(heads), N, d]) in its storage representation."""
-    n = w.Nq if tensor == "q" else w.Nk
+    n = w.Nq if tensor in ("q", "do") else w.Nk
     store = np.uint16 if w.dtype == "bf16" else np.float16
     if heads is not None:
         out = np.empty((len(heads), n, w.d), dtype=store)

@@ -1,9 +1,10 @@
-"""MI355X (gfx950) FlashAttention forward: C-ABI library + thin binding.
+"""MI355X (gfx950) FlashAttention: C-ABI library + thin binding.
 
-The compute path is libattn_mi355x.so (hand-written HIP kernels); this
-package only marshals torch tensors into its C entry points.
+The compute path is libattn_mi355x.so (hand-written HIP kernels for the
+forward pass, its split-KV decode and quantised variants, and the backward
+pass); this package only marshals torch tensors into its C entry points.
 """
 from .binding import (  # noqa: F401
-    ATTN_BF16, ATTN_FP16, attn_fwd, attn_fwd_decode, attn_fwd_q8, build_info, debug_cvt_e4m3, debug_qk_i32,
-    decode_splits, lib, quantize_rows_i8, quantize_tensor_e4m3, status_str, workspace_bytes,
+    ATTN_BF16, ATTN_FP16, attn_bwd, attn_fwd, attn_fwd_decode, attn_fwd_q8, build_info, debug_cvt_e4m3,
+    debug_qk_i32, decode_splits, lib, quantize_rows_i8, quantize_tensor_e4m3, status_str, workspace_bytes,
 )

@@ -25,6 +25,8 @@ SIGNATURES = {
     "attn_fwd_decode_splits": (_I, [_I, _I, _I, _I]),
     "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "attn_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
     "attn_quantize_rows_i8": (_I, [_P, _P, _P, _L, _I, _P]),
     "attn_quantize_e4m3_workspace_bytes": (_Z, [_L]),
     "attn_quantize_tensor_e4m3": (_I, [_P, _P, _P, _L, _P, _Z, _P]),
@@ -125,6 +127,33 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
                         workspace.numel() if workspace is not None else 0, _stream())
     _check(rc, "attn_fwd")
     return out, lse
+
+
+def attn_bwd(q, k, v, out, dout, lse, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """dQ, dK, dV of sum(dout * out) for out, lse = attn_fwd(q, k, v, causal, scale)."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, out, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise ValueError("q, k, v, out, dout must share one dtype")
+    if lse is None or lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be the [B, H, Nq] float32 log-sum-exp of the forward")
+    code = _dtype_code(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    wsb = int(lib().attn_bwd_workspace_bytes(B, H, Nq, Nk, d, code))
+    if workspace is None:
+        workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
+    rc = lib().attn_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
+                        _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, H, Nq, Nk, d, scale,
+                        int(bool(causal)), code, _dev(workspace, "workspace"), workspace.numel(), _stream())
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
 
 
 def decode_splits(B, H, Nk, d) -> int:

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn_mi355x.so")
-SOURCES = ["prefill.hip", "decode.hip", "quant.hip", "api.hip"]
+SOURCES = ["prefill.hip", "decode.hip", "quant.hip", "bwd.hip", "api.hip"]
 ARCH = "gfx950"
 
 

@@ -91,6 +91,31 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
+  (void)Nk;
+  (void)d;
+  (void)dtype;
+  if (B < 1 || H < 1 || Nq < 1) return 0;
+  return attn::bwd_workspace_bytes(B, H, Nq);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(q, k, v, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !lse || !dq || !dk || !dv) return ATTN_E_INVALID;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_E_INVALID;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (!prefill_head_ok(Nq, Nk, d) || !prefill_grid_ok(B, H, Nk)) return ATTN_E_INVALID;
+  if ((long long)Nq * 8 > (long long)UINT32_MAX) return ATTN_E_INVALID;
+  if (!workspace || workspace_bytes < attn::bwd_workspace_bytes(B, H, Nq) || !aligned16(workspace))
+    return ATTN_E_WORKSPACE;
+  return hip_status(attn::launch_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal != 0,
+                                     dtype == ATTN_BF16, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int attn_quantize_rows_i8(const void* x, int8_t* x8, float* scales, long rows, int d, void* stream) {
   if (!x || !x8 || !scales || rows < 1) return ATTN_E_INVALID;
   if (!aligned16(x) || !aligned16(x8) || !aligned4(scales)) return ATTN_E_INVALID;
@@ -156,7 +181,9 @@ const char* attn_build_info(void) {
          "softmax phases, 32 rows/wave), BN=64 (d=128) / 128 (d=64), direct-to-LDS K/V tiles, 32x32x16 MFMA, "
          "S^T=KQ^T, V^T via ds_read_b64_tr_b16, rescale threshold 2^8, causal blocks paired on large grids; "
          "decode split-KV 256 threads, 8 rows in flight/lane + LSE merge; "
-         "q8 prefill d=128 BM=128 BN=64, int8 32x32x32 + fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8";
+         "q8 prefill d=128 BM=128 BN=64, int8 32x32x32 + fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8; "
+         "backward: (lse, D) preprocess, dK/dV kernel (128 keys/WG, 32-query steps, K and V rows resident), "
+         "dQ kernel (128 queries/WG, 32-key steps), no atomics";
 }
 
 }  // extern "C"

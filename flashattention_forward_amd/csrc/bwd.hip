@@ -1,0 +1,554 @@
+// Backward pass of attention for gfx950 (bf16/fp16, d in {64, 128}): the
+// gradients dQ, dK, dV of sum(dO * O), recomputing the probability tiles from
+// Q, K and the forward's log-sum-exp instead of storing them ("Backward:
+// recompute instead of store" in the marketmaker.cc post "Can a full trading
+// day of context beat one minute? Flash attention and the sequence-length
+// question").  With P = softmax(scale Q K^T) (future keys masked when causal):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = rowsum(dO_i * O_i),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// D_i equals rowsum(P_i * dP_i) (both are dO_i . O_i); it is computed once per
+// row from the stored O.
+//
+// Three kernels, no atomics:
+//   bwd_pre: per query row, (LSE log2 e, D) into a float2 workspace;
+//   bwd_kv:  a workgroup owns 128 keys (32 per wave, K and V held in registers
+//            as MFMA operands) and streams the queries in steps of 32 through
+//            LDS (Q, dO tiles and their (LSE, D) pairs, double-buffered,
+//            loaded straight into LDS).  Per step and wave: S = Q K^T and
+//            dP = dO V^T come out with one key per lane, which is exactly the
+//            A-operand layout of P^T and dS^T, so dV += P^T dO and
+//            dK += dS^T Q follow with dO and Q read transposed from LDS;
+//   bwd_dq:  a workgroup owns 128 queries (Q and dO in registers) and streams
+//            K and V tiles; S^T = K Q^T and dP^T = V dO^T come out with one
+//            query per lane, the A-operand layout of dS, and dQ += dS K reads
+//            K transposed from LDS.
+// S and dP are thus computed twice (7 matrix products instead of 5) in
+// exchange for no cross-workgroup reduction.
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace attn {
+
+namespace {
+
+template <int D>
+struct BwdCfg {
+  static constexpr int ROWB = 2 * D;               // bytes per row
+  static constexpr int SPR = ROWB / 16;            // 16-byte slots per row
+  static constexpr int RPI = 1024 / ROWB;          // rows per 1 KB wave load
+  static constexpr int NW = 4;                     // waves per workgroup
+  static constexpr int BO = 32 * NW;               // rows owned by a workgroup (32 per wave)
+  static constexpr int BS = 32;                    // rows streamed per step
+  static constexpr int TILEB = BS * ROWB;          // bytes per streamed tile
+  static constexpr int LPW = TILEB / 1024 / NW;    // 1 KB loads per wave per tile
+  static constexpr int KSTEPS = D / 16;            // MFMA k-steps over d
+  static constexpr int NBD = D / 32;               // 32-column blocks of d
+};
+
+// XOR swizzle of the 16-byte slots of a streamed tile row.  Conflict-free for
+// both access patterns of these tiles: row reads (ds_read_b128, 16 consecutive
+// rows at one logical slot) and transposing reads (ds_read_b64_tr_b16, 4
+// consecutive rows x 64 bytes).  It depends on the row's low 4 bits only, so
+// rows 16 apart share it.
+template <int D>
+__device__ __forceinline__ int bswz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+__device__ __forceinline__ void bwd_load_lds16(const __amdgpu_buffer_rsrc_t& r, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void bwd_load_lds4(const __amdgpu_buffer_rsrc_t& r, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)dst, 4, voff, 0, 0, 0);
+}
+
+template <class M>
+__device__ __forceinline__ typename M::op8 pack8(const f32x16& x, int base) {
+  typedef typename M::op2 op2;
+  const op2 a = M::pack2(x[base + 0], x[base + 1]), b = M::pack2(x[base + 2], x[base + 3]);
+  const op2 e = M::pack2(x[base + 4], x[base + 5]), f = M::pack2(x[base + 6], x[base + 7]);
+  return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3), __builtin_shufflevector(e, f, 0, 1, 2, 3),
+                                 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint16_t to_half_bits(float x) {
+  typedef typename Mfma<BF16>::op2 op2;
+  const op2 p = Mfma<BF16>::pack2(x, 0.f);
+  return __builtin_bit_cast(uint32_t, p) & 0xffffu;
+}
+
+// ---------------------------------------------------------------- bwd_pre
+// One row per D/8 lanes (16 bytes each): D_i = sum_c dO_ic O_ic in fp32 and
+// the log-sum-exp in base 2.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ LSE, float2* __restrict__ LD,
+                                                      long rows) {
+  constexpr int TPR = D / 8;
+  const long row = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = *reinterpret_cast<const u32x4*>(O + row * D + part * 8);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + part * 8);
+    const f16x8 oh = __builtin_bit_cast(f16x8, o), gh = __builtin_bit_cast(f16x8, g);
+    // widen each 16-bit pair exactly to fp32 (the products are exact in fp32)
+    // and keep the two halves of each pair in separate sums: a single chain
+    // over both halves is fused by the compiler into a packed dot product
+    // that, on this target, reads the first 32-bit word of the row chunk
+    // four times
+    float acc1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float o0, o1, g0, g1;
+      if (BF16) {
+        o0 = __builtin_bit_cast(float, o[j] << 16);
+        o1 = __builtin_bit_cast(float, o[j] & 0xffff0000u);
+        g0 = __builtin_bit_cast(float, g[j] << 16);
+        g1 = __builtin_bit_cast(float, g[j] & 0xffff0000u);
+      } else {
+        o0 = (float)oh[2 * j];
+        o1 = (float)oh[2 * j + 1];
+        g0 = (float)gh[2 * j];
+        g1 = (float)gh[2 * j + 1];
+      }
+      acc = fmaf(o0, g0, acc);
+      acc1 = fmaf(o1, g1, acc1);
+    }
+    acc += acc1;
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && part == 0) LD[row] = make_float2(LSE[row] * kLog2e, acc);
+}
+
+// ---------------------------------------------------------------- bwd_kv
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int Nq, int Nk, float c, float scale, int nkb, int total) {
+  using C = BwdCfg<D>;
+  using M = Mfma<BF16>;
+  typedef typename M::op8 op8;
+  __shared__ __attribute__((aligned(1024))) char q0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char q1s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char d0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char d1s[C::TILEB];
+  __shared__ __attribute__((aligned(256))) char l0s[C::BS * 8];
+  __shared__ __attribute__((aligned(256))) char l1s[C::BS * 8];
+  // at d = 128 each wave's V rows live in LDS (same swizzled row layout as the
+  // streamed tiles) instead of 32 more registers
+  constexpr bool VLDS = D == 128;
+  __shared__ __attribute__((aligned(1024))) char vws[VLDS ? C::NW * 32 * C::ROWB : 16];
+
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int bh = logical / nkb;
+  const int k0 = (logical - bh * nkb) * C::BO;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int off = Nk - Nq;  // bottom-right causal alignment
+  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
+  const auto rdo = make_rsrc(dO + qbase, (uint32_t)Nq * D * 2);
+  const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
+  const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
+  const auto rld = make_rsrc(LD + (size_t)bh * Nq, (uint32_t)Nq * 8);
+
+  // this wave's keys: K and V rows as B operands (n = key, k = d)
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + l32;
+  op8 kop[C::KSTEPS], vop[VLDS ? 1 : C::KSTEPS];
+  char* const vw = vws + (VLDS ? w * 32 * C::ROWB : 0);
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    kop[kk] = __builtin_bit_cast(op8, buf_load16(rk, (uint32_t)key * C::ROWB + (16 * kk + 8 * h) * 2));
+    const u32x4 x = buf_load16(rv, (uint32_t)key * C::ROWB + (16 * kk + 8 * h) * 2);
+    if (VLDS)
+      lds_store<u32x4>(vw, l32 * C::ROWB + 16 * ((2 * kk + h) ^ bswz<D>(l32)), x);
+    else
+      vop[kk < (VLDS ? 1 : C::KSTEPS) ? kk : 0] = __builtin_bit_cast(op8, x);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // tile loads: wave w fills 1 KB blocks LPW w .. LPW w + LPW-1 of a Q and a dO tile
+  uint32_t goff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int row = (C::LPW * w + i) * C::RPI + lane / C::SPR, ps = lane % C::SPR;
+    goff[i] = (uint32_t)row * C::ROWB + 16 * (ps ^ bswz<D>(row));
+  }
+  auto issue = [&](int st, char* qt, char* dt, char* lt) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(st * C::BS) * C::ROWB;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      bwd_load_lds16(rq, qt + 1024 * (C::LPW * w + i), base + goff[i]);
+      bwd_load_lds16(rdo, dt + 1024 * (C::LPW * w + i), base + goff[i]);
+    }
+    if (w == 0) bwd_load_lds4(rld, lt, (uint32_t)(st * C::BS) * 8 + 4 * lane);
+  };
+  // row reads (A operand: m = query l32, k = d 16 kk + 8h .. +7): byte offset
+  // l32 ROWB + ((32 kk + 16 h) ^ 16 swz(l32)), one XOR-add per read
+  const uint32_t ra_base = l32 * C::ROWB, ra_x = 16 * (h ^ bswz<D>(l32));
+  // transposing reads (B operand: k = queries {4h..4h+3, 8+4h..8+4h+3} (+16 t), n = d 32 nb + l32)
+  // lane r16 of each 16 points at row (r16/4) + 4h (+ 8 for the upper half,
+  // + 16 ti), columns 32 nb + 16 g1 + 4 (r16%4) .. +3: byte offset
+  // tr_base[hi] + ((64 nb) ^ tr_x[hi]) + 32 ti ROWB, with the swizzle folded into tr_x
+  uint32_t tr_base[2], tr_x[2];
+  {
+    const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = (r16 >> 2) + 4 * h + 8 * hi;
+      tr_base[hi] = row * C::ROWB + 8 * (r16 & 1);
+      tr_x[hi] = 16 * ((2 * g1 + ((r16 & 3) >> 1)) ^ bswz<D>(row));
+    }
+  }
+  auto tr_load = [&](const char* t, int nb, int ti) __attribute__((always_inline)) {
+    const s16x4 lo = lds_read_tr16(t, tr_base[0] + ((64u * nb) ^ tr_x[0]) + 16 * ti * C::ROWB);
+    const s16x4 hi = lds_read_tr16(t, tr_base[1] + ((64u * nb) ^ tr_x[1]) + 16 * ti * C::ROWB);
+    return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 dv[C::NBD], dk[C::NBD];
+#pragma unroll
+  for (int nb = 0; nb < C::NBD; ++nb) {
+    dv[nb] = f32x16{};
+    dk[nb] = f32x16{};
+  }
+
+  // acc += A B over the KSTEPS k-steps: A = rows of tile t (two k-steps ahead),
+  // B = bop (registers) or, with BL, this wave's LDS rows, which share the A
+  // rows' offsets
+  auto row_gemm = [&](auto BL, const char* t, const op8* bop, const char* bl, f32x16 acc)
+                      __attribute__((always_inline)) {
+    constexpr bool FROM_LDS = decltype(BL)::value;
+    op8 ar[2], br[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      ar[kk] = lds_load<op8>(t, ra_base + ((32u * kk) ^ ra_x));
+      if (FROM_LDS) br[kk] = lds_load<op8>(bl, ra_base + ((32u * kk) ^ ra_x));
+    }
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      const op8 x = ar[kk & 1];
+      const op8 y = FROM_LDS ? br[kk & 1] : bop[FROM_LDS ? 0 : kk];
+      if (kk + 2 < C::KSTEPS) {
+        ar[kk & 1] = lds_load<op8>(t, ra_base + ((32u * (kk + 2)) ^ ra_x));
+        if (FROM_LDS) br[kk & 1] = lds_load<op8>(bl, ra_base + ((32u * (kk + 2)) ^ ra_x));
+      }
+      acc = M::mma(x, y, acc);
+    }
+    constexpr int NR = FROM_LDS ? 2 : 1;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NR, 0);
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (kk + 2 < C::KSTEPS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
+    }
+    return acc;
+  };
+  // acc[nb] += A[ti] * (tile t read transposed), B operands two ahead
+  auto tr_gemm = [&](const char* t, const op8* am, f32x16* acc) __attribute__((always_inline)) {
+    constexpr int NT = 2 * C::NBD;
+    op8 br[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) br[u] = tr_load(t, u % C::NBD, u / C::NBD);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const op8 x = br[u & 1];
+      if (u + 2 < NT) br[u & 1] = tr_load(t, (u + 2) % C::NBD, (u + 2) / C::NBD);
+      acc[u % C::NBD] = M::mma(am[u / C::NBD], x, acc[u % C::NBD]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (u + 2 < NT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+  };
+
+  // step: queries q0 .. q0+31 from tiles qt, dt, lt.  Element i of S, dP:
+  // query q0 + 8 (i/4) + 4h + i%4 of this lane's key.
+  auto step = [&](int st, const char* qt, const char* dt, const char* lt) __attribute__((always_inline)) {
+    const int q0 = st * C::BS;
+    const bool edge = (q0 + C::BS > Nq) || (CAUSAL && kw0 + 31 > q0 + off);
+    // P = exp2(S c - LSE log2 e), masked; kept only as the 16-bit MFMA operand
+    op8 pa[2];
+    {
+      f32x16 sv = row_gemm(std::false_type{}, qt, kop, nullptr, f32x16{});
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 x0 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8);
+        const f32x4 x1 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8 + 16);
+        const float Lr[4] = {x0[0], x0[2], x1[0], x1[2]};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * a + b;
+          float p = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -Lr[b]));
+          if (edge) {
+            const int qi = q0 + 8 * a + 4 * h + b;
+            if (qi >= Nq || (CAUSAL && key > qi + off)) p = 0.f;
+          }
+          sv[i] = p;
+        }
+      }
+      pa[0] = pack8<M>(sv, 0);
+      pa[1] = pack8<M>(sv, 8);
+    }
+    // the phases stay in order: overlapping them only raises the register peak
+    __builtin_amdgcn_sched_barrier(0);
+    // dV += P^T dO
+    tr_gemm(dt, pa, dv);
+    __builtin_amdgcn_sched_barrier(0);
+    // dS = P (dP - D), from the 16-bit P; dK += dS^T Q
+    op8 da[2];
+    {
+      f32x16 dpv = row_gemm(std::integral_constant<bool, VLDS>{}, dt, vop, vw, f32x16{});
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 x0 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8);
+        const f32x4 x1 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8 + 16);
+        const float Dr[4] = {x0[1], x0[3], x1[1], x1[3]};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * a + b;
+          const float p = (float)pa[i >> 3][i & 7];
+          dpv[i] = p * (dpv[i] - Dr[b]);
+        }
+      }
+      da[0] = pack8<M>(dpv, 0);
+      da[1] = pack8<M>(dpv, 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tr_gemm(qt, da, dk);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // queries that see at least one of this workgroup's keys
+  int s0 = 0;
+  if (CAUSAL) s0 = max(0, k0 - off) / C::BS;
+  const int ns = (Nq + C::BS - 1) / C::BS;
+  issue(s0, q0s, d0s, l0s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = s0; st < ns; ++st) {
+    const bool odd = (st - s0) & 1;
+    if (st + 1 < ns) issue(st + 1, odd ? q0s : q1s, odd ? d0s : d1s, odd ? l0s : l1s);
+    step(st, odd ? q1s : q0s, odd ? d1s : d0s, odd ? l1s : l0s);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // element i of block nb: key kw0 + 8 (i/4) + 4h + i%4, column 32 nb + l32
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kr = kw0 + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (kr < Nk) {
+      uint16_t* pv = dV + kbase + (size_t)kr * D + l32;
+      uint16_t* pk = dK + kbase + (size_t)kr * D + l32;
+#pragma unroll
+      for (int nb = 0; nb < C::NBD; ++nb) {
+        pv[32 * nb] = to_half_bits<BF16>(dv[nb][i]);
+        pk[32 * nb] = to_half_bits<BF16>(dk[nb][i] * scale);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_dq
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dQ, int Nq, int Nk,
+    float c, float scale, int nqb, int total) {
+  using C = BwdCfg<D>;
+  using M = Mfma<BF16>;
+  typedef typename M::op8 op8;
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
+
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int bh = logical / nqb;
+  int qb = logical - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest query blocks first
+  const int q0 = qb * C::BO;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int off = Nk - Nq;
+  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
+  const auto rdo = make_rsrc(dO + qbase, (uint32_t)Nq * D * 2);
+  const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
+  const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
+
+  // this wave's queries: Q and dO rows as B operands (n = query, k = d)
+  const int qw0 = q0 + 32 * w;
+  const int query = qw0 + l32;
+  op8 qop[C::KSTEPS], dop[C::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)query * C::ROWB + (16 * kk + 8 * h) * 2));
+    dop[kk] = __builtin_bit_cast(op8, buf_load16(rdo, (uint32_t)query * C::ROWB + (16 * kk + 8 * h) * 2));
+  }
+  float Lq = 0.f, Dq = 0.f;
+  if (query < Nq) {
+    const float2 x = LD[(size_t)bh * Nq + query];
+    Lq = x.x;
+    Dq = x.y;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint32_t goff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int row = (C::LPW * w + i) * C::RPI + lane / C::SPR, ps = lane % C::SPR;
+    goff[i] = (uint32_t)row * C::ROWB + 16 * (ps ^ bswz<D>(row));
+  }
+  auto issue = [&](int st, char* kt, char* vt) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(st * C::BS) * C::ROWB;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      bwd_load_lds16(rk, kt + 1024 * (C::LPW * w + i), base + goff[i]);
+      bwd_load_lds16(rv, vt + 1024 * (C::LPW * w + i), base + goff[i]);
+    }
+  };
+  uint32_t ra[C::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) ra[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ bswz<D>(l32));
+  // lane r16 of each 16 points at row (r16/4) + 4h (+ 8 for the upper half,
+  // + 16 ti), columns 32 nb + 16 g1 + 4 (r16%4) .. +3: byte offset
+  // tr_base[hi] + ((64 nb) ^ tr_x[hi]) + 32 ti ROWB, with the swizzle folded into tr_x
+  uint32_t tr_base[2], tr_x[2];
+  {
+    const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = (r16 >> 2) + 4 * h + 8 * hi;
+      tr_base[hi] = row * C::ROWB + 8 * (r16 & 1);
+      tr_x[hi] = 16 * ((2 * g1 + ((r16 & 3) >> 1)) ^ bswz<D>(row));
+    }
+  }
+  auto tr_load = [&](const char* t, int nb, int ti) __attribute__((always_inline)) {
+    const s16x4 lo = lds_read_tr16(t, tr_base[0] + ((64u * nb) ^ tr_x[0]) + 16 * ti * C::ROWB);
+    const s16x4 hi = lds_read_tr16(t, tr_base[1] + ((64u * nb) ^ tr_x[1]) + 16 * ti * C::ROWB);
+    return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 dq[C::NBD];
+#pragma unroll
+  for (int nb = 0; nb < C::NBD; ++nb) dq[nb] = f32x16{};
+
+  // step: keys j0 .. j0+31 from tiles kt, vt
+  auto step = [&](int st, const char* kt, const char* vt) __attribute__((always_inline)) {
+    const int j0 = st * C::BS;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      s = M::mma(lds_load<op8>(kt, ra[kk]), qop[kk], s);
+      dp = M::mma(lds_load<op8>(vt, ra[kk]), dop[kk], dp);
+    }
+    // element i: key j0 + 8 (i/4) + 4h + i%4 of this lane's query
+    const bool edge = (j0 + C::BS > Nk) || (CAUSAL && j0 + 31 > qw0 + off);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -Lq));
+      if (edge) {
+        const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (kj >= Nk || (CAUSAL && kj > query + off)) p = 0.f;
+      }
+      dp[i] = p * (dp[i] - Dq);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const op8 da = pack8<M>(dp, 8 * ti);
+#pragma unroll
+      for (int nb = 0; nb < C::NBD; ++nb) dq[nb] = M::mma(da, tr_load(kt, nb, ti), dq[nb]);
+    }
+  };
+
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = min(Nk, min(q0 + C::BO, Nq) - 1 + off + 1);
+  const int ns = (kv_end + C::BS - 1) / C::BS;
+  issue(0, k0s, v0s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = 0; st < ns; st += 2) {
+    if (st + 1 < ns) issue(st + 1, k1s, v1s);
+    step(st, k0s, v0s);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (st + 1 < ns) {
+      if (st + 2 < ns) issue(st + 2, k0s, v0s);
+      step(st + 1, k1s, v1s);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  // element i of block nb: query qw0 + 8 (i/4) + 4h + i%4, column 32 nb + l32
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int qr = qw0 + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (qr < Nq) {
+      uint16_t* pq = dQ + qbase + (size_t)qr * D + l32;
+#pragma unroll
+      for (int nb = 0; nb < C::NBD; ++nb) pq[32 * nb] = to_half_bits<BF16>(dq[nb][i] * scale);
+    }
+  }
+}
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, float scale,
+                        void* workspace, hipStream_t stream) {
+  using C = BwdCfg<D>;
+  float2* ld = static_cast<float2*>(workspace);
+  const long rows = (long)B * H * Nq;
+  constexpr int RPB = 256 / (D / 8);  // rows per bwd_pre block
+  hipLaunchKernelGGL((bwd_pre_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, ld, rows);
+  const float c = scale * kLog2e;
+  const int nkb = (Nk + C::BO - 1) / C::BO;
+  const int totk = nkb * B * H;
+  hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, CAUSAL>), dim3(totk), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
+                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Nq, Nk, c, scale, nkb, totk);
+  const int nqb = (Nq + C::BO - 1) / C::BO;
+  const int totq = nqb * B * H;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL>), dim3(totq), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
+                     static_cast<uint16_t*>(dq), Nq, Nk, c, scale, nqb, totq);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int Nq) { return (size_t)B * H * Nq * sizeof(float2); }
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, bool causal,
+                      bool bf16, void* workspace, hipStream_t stream) {
+#define ATTN_BWD(D_, BF_, CA_)                                                                                   \
+  if (d == D_ && bf16 == BF_ && causal == CA_)                                                                   \
+    return launch_bwd_t<D_, BF_, CA_>(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, scale, workspace, stream);
+  ATTN_BWD(128, true, false)
+  ATTN_BWD(128, true, true)
+  ATTN_BWD(128, false, false)
+  ATTN_BWD(128, false, true)
+  ATTN_BWD(64, true, false)
+  ATTN_BWD(64, true, true)
+  ATTN_BWD(64, false, false)
+  ATTN_BWD(64, false, true)
+#undef ATTN_BWD
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

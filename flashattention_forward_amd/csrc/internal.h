@@ -19,6 +19,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
                          int B, int H, int Nk, int d, float scale, bool bf16, int splits,
                          void* workspace, hipStream_t stream);
 
+// Backward pass: preprocess (log-sum-exp in base 2, rowsum(dO * O)) into a
+// float2 [B, H, Nq] workspace, then the dK/dV and dQ kernels.
+size_t bwd_workspace_bytes(int B, int H, int Nq);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, bool causal,
+                      bool bf16, void* workspace, hipStream_t stream);
+
 // Quantisation kernels and the quantised forward.
 hipError_t launch_quantize_rows_i8(const void* x, int8_t* x8, float* scales, long rows, int d,
                                    hipStream_t stream);

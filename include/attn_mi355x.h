@@ -1,6 +1,7 @@
 /*
- * attn_mi355x.h -- C ABI of the MI355X (gfx950) FlashAttention forward library
- * (libattn_mi355x.so).
+ * attn_mi355x.h -- C ABI of the MI355X (gfx950) FlashAttention library
+ * (libattn_mi355x.so): the forward pass (prefill, split-KV decode, quantised)
+ * and its backward pass.
  *
  * What the library computes.  For every batch b and head h, exact attention
  *     O = softmax(Q K^T * scale) V
@@ -14,7 +15,8 @@
  * writes the per-row log-sum-exp
  *     LSE[b,h,i] = ln sum_{j visible} exp(scale * q_i . k_j)
  * (natural log; the stored softmax statistics (m, l) of "Backward: recompute
- * instead of store", folded as m + ln l).
+ * instead of store", folded as m + ln l), which attn_bwd takes back to
+ * rebuild the probabilities for the gradients.
  *
  * Conventions shared by every entry point:
  *   - Tensors are dense, row-major [B, H, N, d] (batch, heads, sequence,
@@ -108,6 +110,33 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* out, float* lse,
                     int B, int H, int Nk, int d, float scale, int dtype, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention backward: the gradients of sum(dout * out) with respect to q, k
+ * and v, for out = attention(q, k, v) as computed by attn_fwd (same scale and
+ * causal flag).  The probability tiles are rebuilt from q, k and the
+ * forward's log-sum-exp instead of being stored ("Backward: recompute
+ * instead of store" in the marketmaker.cc post "Can a full trading day of
+ * context beat one minute?"): with P = softmax(scale q k^T) (future keys
+ * masked when causal), dV = P^T dO, dP = dO V^T, dS = P * (dP - D) with
+ * D_i = sum_c dO_ic O_ic, dQ = scale dS K, dK = scale dS^T Q.
+ *   q, k, v, out, dout as in attn_fwd ([B,H,N,d], dtype); lse [B,H,Nq]
+ *   float32 (natural log) from attn_fwd, required.
+ *   dq [B,H,Nq,d], dk, dv [B,H,Nk,d] (dtype), fully overwritten; fp32
+ *   accumulation, rounded to nearest even.
+ *   workspace: device buffer of at least attn_bwd_workspace_bytes() bytes
+ *   (B*H*Nq float pairs: lse in base 2 and D), 16-byte aligned; its contents
+ *   after the call are unspecified.
+ *   d in {64, 128}; B, H, Nq, Nk >= 1; causal needs Nq <= Nk; one head of
+ *   q, k, v stays below 2^32 bytes (ATTN_E_INVALID otherwise).
+ * Three kernels run on `stream`: the (lse, D) preprocess, a key-block kernel
+ * for dK and dV and a query-block kernel for dQ.  No atomics: the result does
+ * not depend on scheduling.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Quantisation of bf16 inputs for the quantised forward (token-level INT8

@@ -111,6 +111,35 @@ def test_quant_entry_points_reject():
     assert L.attn_debug_cvt_e4m3(A, A, 3, None) == Bd.ATTN_E_INVALID
 
 
+def bwd(**kw):
+    a = dict(q=A, k=A, v=A, out=A, do=A, lse=A, dq=A, dk=A, dv=A, B=2, H=3, Nq=40, Nk=50, d=128, scale=0.1,
+             causal=0, dtype=0, ws=A, wsb=1 << 20)
+    a.update(kw)
+    return Bd.lib().attn_bwd(a["q"], a["k"], a["v"], a["out"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                             a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["ws"], a["wsb"],
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), Bd.ATTN_E_INVALID), (dict(do=None), Bd.ATTN_E_INVALID), (dict(lse=None), Bd.ATTN_E_INVALID),
+    (dict(dq=None), Bd.ATTN_E_INVALID), (dict(dk=None), Bd.ATTN_E_INVALID), (dict(dv=None), Bd.ATTN_E_INVALID),
+    (dict(do=MIS), Bd.ATTN_E_INVALID), (dict(dv=MIS), Bd.ATTN_E_INVALID), (dict(lse=A + 2), Bd.ATTN_E_INVALID),
+    (dict(B=0), Bd.ATTN_E_INVALID), (dict(Nk=0), Bd.ATTN_E_INVALID), (dict(scale=0.0), Bd.ATTN_E_INVALID),
+    (dict(causal=1, Nq=51), Bd.ATTN_E_INVALID), (dict(Nk=2 ** 24), Bd.ATTN_E_INVALID),
+    (dict(d=96), Bd.ATTN_E_UNSUPPORTED), (dict(dtype=3), Bd.ATTN_E_UNSUPPORTED),
+    (dict(ws=None), Bd.ATTN_E_WORKSPACE), (dict(wsb=2 * 3 * 40 * 8 - 1), Bd.ATTN_E_WORKSPACE),
+    (dict(ws=MIS), Bd.ATTN_E_WORKSPACE),
+])
+def test_attn_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_size():
+    L = Bd.lib()
+    assert L.attn_bwd_workspace_bytes(4, 32, 4096, 4096, 128, 0) == 4 * 32 * 4096 * 8
+    assert L.attn_bwd_workspace_bytes(0, 1, 1, 1, 64, 0) == 0
+
+
 def test_status_strings_and_build_info():
     for c in (0, -1, -2, -3, -4):
         assert Bd.status_str(c) and Bd.status_str(c) != "unknown status"
