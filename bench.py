@@ -14,9 +14,10 @@ Printed as ONE JSON line, which also carries
     source (null otherwise);
   * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
     workload on this host's cores;
-  * other_workloads: the long causal fp16 sequence, the split-KV decode
-    (GB/s over the K+V bytes) and the quantised forward, each timed the same
-    way (informational).
+  * other_workloads: the long causal fp16 sequence, the backward pass at the
+    prefill configuration (algorithmic FLOPs of its five matrix products,
+    2.5x the forward's), the split-KV decode (GB/s over the K+V bytes) and the
+    quantised forward, each timed the same way (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
                        [--copy-calibration]
@@ -267,6 +268,24 @@ def main():
         other["long_23400_causal"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(wl.flops() / per[0] / 1e12, 3),
                                       "frac_peak": round(wl.flops() / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del tq, tk, tv, o, l
+        # backward pass at the prefill configuration: algorithmic FLOPs of its five
+        # products (Q K^T, P^T dO, dO V^T, dS K, dS^T Q) = 2.5x the forward's
+        tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(w, threads=16))
+        tdo = G.to_torch(G.draw_tensor(w, "do", threads=16), "bf16")
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(w.B * w.H * w.Nq * 8, device="cuda", dtype=torch.uint8)
+        for causal in (False, True):
+            o, l = F.attn_fwd(tq, tk, tv, causal=causal, scale=w.scale)
+            _, per = timed_launches([lambda: F.attn_bwd(tq, tk, tv, o, tdo, l, causal=causal, scale=w.scale, dq=dq,
+                                                        dk=dk, dv=dv, workspace=ws)],
+                                    max(5, args.steps // 2), args.warmup)
+            fl = 2.5 * (flops_c if causal else flops_nc)
+            other["backward_4k_causal" if causal else "backward_4k"] = {
+                "ms": round(per[0] * 1e3, 4), "tflops": round(fl / per[0] / 1e12, 3),
+                "frac_peak": round(fl / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": fl}
+            del o, l
+        del tq, tk, tv, tdo, dq, dk, dv, ws
+        torch.cuda.empty_cache()
         # split-KV decode
         wd = G.WORKLOADS["decode_8k"]
         tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(wd, threads=16))
