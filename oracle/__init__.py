@@ -32,7 +32,9 @@ Modules:
                  quantised-attention oracle.
   backward    -- the gradients dQ, dK, dV of attention by the chain rule
                  through the plain definition.
+  variants    -- grouped-query heads (GQA/MQA) and packed variable-length
+                 batches, by head mapping and slicing of the definition.
 
 Parity status of every function is stated in its module header.
 """
-from . import attention, backward, quant, recurrence  # noqa: F401
+from . import attention, backward, quant, recurrence, variants  # noqa: F401

@@ -419,3 +419,101 @@ def pin_bwd_causal_first_row(bwd, tol=1e-12):
 
 
 BACKWARD_PINS = [pin_bwd_torch, pin_bwd_uniform, pin_bwd_sums, pin_bwd_key_shift, pin_bwd_causal_first_row]
+
+
+# ---------------------------------------------------------------- GQA / varlen
+#
+# ``gqa(q, k, v, scale, causal) -> (O, LSE)`` on [B, H, N, d] / [B, Hkv, N, d];
+# ``varlen(q, k, v, cu_q, cu_k, scale, causal) -> (O, LSE)`` on [H, total, d].
+
+def pin_gqa_repeat(gqa, tol=1e-13):
+    """GQA equals plain multi-head attention with every K/V head repeated for
+    its H/Hkv query heads (np.repeat along the head axis), MQA included."""
+    for (B, H, Hkv, Nq, Nk, causal) in [(2, 4, 2, 5, 7, False), (1, 6, 3, 6, 6, True), (1, 4, 1, 3, 9, True),
+                                        (1, 3, 3, 4, 4, False)]:
+        q, k, v = _rand(B, H, Nq, 3), _rand(B, Hkv, Nk, 3), _rand(B, Hkv, Nk, 2)
+        O, L = gqa(q, k, v, 0.6, causal)
+        from oracle import attention as A
+        Od, Ld = A.attention(q, np.repeat(k, H // Hkv, axis=1), np.repeat(v, H // Hkv, axis=1), 0.6, causal)
+        assert np.max(np.abs(O - Od)) <= tol and np.max(np.abs(L - Ld)) <= tol
+
+
+def pin_gqa_torch(gqa, tol=1e-12):
+    """torch's CPU float64 scaled_dot_product_attention with enable_gqa
+    (library), bottom-right causal via causal_lower_right."""
+    from torch.nn.attention.bias import causal_lower_right
+    for (B, H, Hkv, Nq, Nk, causal) in [(2, 8, 2, 6, 9, False), (1, 4, 2, 7, 7, True), (1, 6, 1, 5, 11, True)]:
+        q, k, v = _rand(B, H, Nq, 4), _rand(B, Hkv, Nk, 4), _rand(B, Hkv, Nk, 4)
+        O, _ = gqa(q, k, v, 0.5, causal)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        mask = causal_lower_right(Nq, Nk) if causal else None
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.5,
+                                                               enable_gqa=True).numpy()
+        assert np.max(np.abs(O - ref)) <= tol
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+
+
+def pin_varlen_per_sequence(varlen, tol=1e-13):
+    """A packed batch equals one plain call per sequence (definition per
+    sequence, its own bottom-right causal alignment), sequences of unequal
+    query and key lengths, GQA heads included."""
+    from oracle import attention as A
+    for (lq, lk, H, Hkv, causal) in [([3, 1, 6], [4, 2, 6], 2, 1, False), ([5, 2, 7], [5, 3, 9], 4, 2, True),
+                                     ([1], [8], 2, 2, True)]:
+        cq, ck = _cu(lq), _cu(lk)
+        q, k, v = _rand(H, cq[-1], 3), _rand(Hkv, ck[-1], 3), _rand(Hkv, ck[-1], 2)
+        O, L = varlen(q, k, v, cq, ck, 0.7, causal)
+        for s in range(len(lq)):
+            for h in range(H):
+                g = h // (H // Hkv)
+                o, l = A.attention_head(q[h, cq[s]:cq[s + 1]], k[g, ck[s]:ck[s + 1]], v[g, ck[s]:ck[s + 1]], 0.7,
+                                        causal)
+                assert np.max(np.abs(O[h, cq[s]:cq[s + 1]] - o)) <= tol
+                assert np.max(np.abs(L[h, cq[s]:cq[s + 1]] - l)) <= tol
+
+
+def pin_varlen_empty_rows(varlen, tol=1e-13):
+    """Rows that see no key (an empty key range, or causal with more queries
+    than keys in a sequence) are the empty sum: O = 0 and LSE = -inf; the
+    other rows are a brute-force softmax over their visible keys."""
+    lq, lk = [2, 5, 0, 3], [0, 3, 4, 3]
+    cq, ck = _cu(lq), _cu(lk)
+    q, k, v = _rand(1, cq[-1], 2), _rand(1, ck[-1], 2), _rand(1, ck[-1], 2)
+    O, L = varlen(q, k, v, cq, ck, 1.1, True)
+    for s in range(len(lq)):
+        for i in range(lq[s]):
+            r = cq[s] + i
+            vis = [ck[s] + j for j in range(lk[s]) if j <= i + lk[s] - lq[s]]
+            if not vis:
+                assert np.all(O[0, r] == 0.0) and L[0, r] == -np.inf
+                continue
+            sc = np.array([1.1 * float(q[0, r] @ k[0, j]) for j in vis])
+            lse = math.log(sum(math.exp(x) for x in sc))
+            o = sum(math.exp(x - lse) * v[0, j] for x, j in zip(sc, vis))
+            assert abs(L[0, r] - lse) <= tol * max(1.0, abs(lse)) and np.max(np.abs(O[0, r] - o)) <= tol
+
+
+def pin_gqa_backward_torch(bwd_gqa, tol=1e-12):
+    """GQA gradients against torch's CPU float64 autograd through
+    repeat_interleave of the K/V heads (library), which sums the shared
+    heads' contributions by itself."""
+    for (B, H, Hkv, Nq, Nk, causal) in [(1, 4, 2, 6, 6, True), (2, 6, 3, 5, 8, False), (1, 4, 1, 7, 7, True)]:
+        q, k, v, do = _rand(B, H, Nq, 3), _rand(B, Hkv, Nk, 3), _rand(B, Hkv, Nk, 3), _rand(B, H, Nq, 3)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        kk = torch.repeat_interleave(tk, H // Hkv, dim=1)
+        vv = torch.repeat_interleave(tv, H // Hkv, dim=1)
+        s = (tq @ kk.transpose(-1, -2)) * 0.8
+        if causal:
+            vis = torch.arange(Nk)[None, :] <= torch.arange(Nq)[:, None] + (Nk - Nq)
+            s = s.masked_fill(~vis, float("-inf"))
+        (torch.softmax(s, dim=-1) @ vv).backward(torch.tensor(do))
+        got = bwd_gqa(q, k, v, do, 0.8, causal)
+        for g, t in zip(got, (tq, tk, tv)):
+            assert np.max(np.abs(g - t.grad.numpy())) <= tol
+
+
+GQA_PINS = [pin_gqa_repeat, pin_gqa_torch]
+VARLEN_PINS = [pin_varlen_per_sequence, pin_varlen_empty_rows]

@@ -1,0 +1,101 @@
+"""GQA and packed variable-length oracles against their pins, and planted
+mistakes in copies of them (no GPU)."""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import variants as V
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.GQA_PINS, ids=lambda f: f.__name__)
+def test_gqa_pins(pin):
+    pin(V.attention_gqa)
+
+
+@pytest.mark.parametrize("pin", P.VARLEN_PINS, ids=lambda f: f.__name__)
+def test_varlen_pins(pin):
+    pin(V.attention_varlen)
+
+
+def test_gqa_backward_pin():
+    P.pin_gqa_backward_torch(V.attention_backward_gqa)
+
+
+def test_kv_head_rejects_uneven_groups():
+    with pytest.raises(ValueError):
+        V.kv_head(0, 6, 4)
+
+
+# ---- planted mistakes: each must fail a pin
+def gqa_variant(q, k, v, scale, causal, mistake=None):
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    O = np.empty(q.shape[:3] + (v.shape[3],))
+    L = np.empty(q.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            g = h % Hkv if mistake == "interleaved_heads" else h // (H // Hkv)
+            O[b, h], L[b, h] = A.attention_head(q[b, h], k[b, g], v[b, g], scale, causal)
+    return O, L
+
+
+def varlen_variant(q, k, v, cu_q, cu_k, scale, causal, mistake=None):
+    H, Hkv = q.shape[0], k.shape[0]
+    O = np.zeros(q.shape[:2] + (v.shape[2],))
+    L = np.full(q.shape[:2], -np.inf)
+    for s in range(len(cu_q) - 1):
+        qa, qb = int(cu_q[s]), int(cu_q[s + 1])
+        ka, kb = int(cu_k[s]), int(cu_k[s + 1])
+        if mistake == "keys_one_short":
+            kb = max(ka, kb - 1)
+        for h in range(H):
+            g = h // (H // Hkv)
+            Nq, Nk = qb - qa, kb - ka
+            if Nq == 0 or Nk == 0:
+                continue
+            if mistake == "top_left_causal":
+                qq, kk, vv = q[h, qa:qb], k[g, ka:kb], v[g, ka:kb]
+                s_ = qq @ kk.T * scale
+                if causal:
+                    s_ = np.where(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None], s_, -np.inf)
+                m = s_.max(axis=1)
+                e = np.exp(s_ - m[:, None])
+                O[h, qa:qb], L[h, qa:qb] = (e @ vv) / e.sum(1)[:, None], m + np.log(e.sum(1))
+                continue
+            O[h, qa:qb], L[h, qa:qb] = V._seq_attention(q[h, qa:qb], k[g, ka:kb], v[g, ka:kb], scale, causal)
+    return O, L
+
+
+def test_unmutated_variant_copies_equal_oracle():
+    rng = np.random.default_rng(4)
+    q, k, v = rng.standard_normal((2, 4, 5, 3)), rng.standard_normal((2, 2, 7, 3)), rng.standard_normal((2, 2, 7, 3))
+    for a, b in zip(gqa_variant(q, k, v, 0.5, True), V.attention_gqa(q, k, v, 0.5, True)):
+        assert np.array_equal(a, b)
+    cq, ck = np.array([0, 3, 7]), np.array([0, 4, 9])
+    q, k, v = rng.standard_normal((2, 7, 3)), rng.standard_normal((1, 9, 3)), rng.standard_normal((1, 9, 3))
+    for a, b in zip(varlen_variant(q, k, v, cq, ck, 0.5, True), V.attention_varlen(q, k, v, cq, ck, 0.5, True)):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("mistake", ["interleaved_heads"])
+def test_gqa_mistake_is_caught(mistake):
+    failed = []
+    for pin in P.GQA_PINS:
+        try:
+            pin(lambda q, k, v, s, c: gqa_variant(q, k, v, s, c, mistake))
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed
+
+
+@pytest.mark.parametrize("mistake", ["keys_one_short", "top_left_causal"])
+def test_varlen_mistake_is_caught(mistake):
+    failed = []
+    for pin in P.VARLEN_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(lambda q, k, v, cq, ck, s, c: varlen_variant(q, k, v, cq, ck, s, c, mistake))
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed
