@@ -50,7 +50,8 @@ class Workload:
         return f / 2.0 if self.causal else f
 
 
-# The five workloads of this project (sizes from the problem statement):
+# The five workloads of this project (sizes from the problem statement), and
+# grouped-query variants of two of them:
 WORKLOADS = {
     # single head smoke case: B=1 H=1 N=256 d=64 bf16 N(0,1), non-causal
     "single_head_256": Workload("single_head_256", 0, 1, 1, 256, 256, 64, "bf16", 1.0, False, 1.0 / 8.0),
@@ -63,6 +64,10 @@ WORKLOADS = {
     "decode_8k": Workload("decode_8k", 3, 64, 32, 1, 8192, 128, "bf16", 1.0, False, 128 ** -0.5),
     # quantised: B=2 H=32 N=8192 d=128, int8 Q/K per token, e4m3 V per tensor
     "quant_8k": Workload("quant_8k", 4, 2, 32, 8192, 8192, 128, "bf16", 1.0, False, 128 ** -0.5),
+    # grouped-query variants of the prefill and decode shapes: 32 query heads on
+    # 8 K/V heads (K/V tensors are drawn with H = 8 via shrink(w, H=8))
+    "gqa_4k_causal": Workload("gqa_4k_causal", 5, 4, 32, 4096, 4096, 128, "bf16", 1.0, True, 128 ** -0.5),
+    "gqa_decode_8k": Workload("gqa_decode_8k", 6, 64, 32, 1, 8192, 128, "bf16", 1.0, False, 128 ** -0.5),
 }
 
 

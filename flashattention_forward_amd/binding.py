@@ -22,6 +22,8 @@ _P, _I, _L, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_floa
 SIGNATURES = {
     "attn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_fwd_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_fwd_decode_splits": (_I, [_I, _I, _I, _I]),
     "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "attn_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
@@ -103,12 +105,14 @@ def workspace_bytes(B, H, Nq, Nk, d, dtype_code) -> int:
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
              workspace=None, want_lse: bool = True):
-    """O, LSE = attention(q, k, v) for [B, H, N, d] bf16/fp16 GPU tensors."""
+    """O, LSE = attention(q, k, v) for [B, H, N, d] bf16/fp16 GPU tensors.
+    k and v may have fewer heads than q (grouped-query attention: query head
+    h reads K/V head h // (H // Hkv))."""
     torch = _torch()
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
-        raise ValueError("q, k, v must be [B, H, N, d] with matching B, H, d and K/V lengths")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != (B, Hkv, Nk, d):
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
     code = _dtype_code(q)
@@ -120,12 +124,41 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     wsb = workspace_bytes(B, H, Nq, Nk, d, code)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
-    rc = lib().attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                        _dev(lse, "lse") if lse is not None else None, B, H, Nq, Nk, d, scale,
-                        int(bool(causal)), code,
-                        _dev(workspace, "workspace") if workspace is not None else None,
-                        workspace.numel() if workspace is not None else 0, _stream())
-    _check(rc, "attn_fwd")
+    args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None]
+    tail = [d, scale, int(bool(causal)), code, _dev(workspace, "workspace") if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _stream()]
+    if Hkv == H:
+        rc = lib().attn_fwd(*args, B, H, Nq, Nk, *tail)
+        _check(rc, "attn_fwd")
+    else:
+        rc = lib().attn_fwd_gqa(*args, B, H, Hkv, Nq, Nk, *tail)
+        _check(rc, "attn_fwd_gqa")
+    return out, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Packed variable-length batch: q [H, total_q, d], k, v [Hkv, total_k, d],
+    cu_seqlens_* int32 GPU tensors of nseq + 1 offsets.  Returns (out, lse)
+    with lse [H, total_q]."""
+    torch = _torch()
+    H, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    if k.shape != (Hkv, total_k, d) or v.shape != (Hkv, total_k, d):
+        raise ValueError("q must be [H, total_q, d] and k, v [Hkv, total_k, d]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total_q), device=q.device, dtype=torch.float32) if lse is None else lse
+    rc = lib().attn_fwd_varlen(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
+                               _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), nseq,
+                               int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, H, Hkv, d, scale,
+                               int(bool(causal)), _dtype_code(q), _stream())
+    _check(rc, "attn_fwd_varlen")
     return out, lse
 
 

@@ -41,6 +41,39 @@ int check_common(const void* q, const void* k, const void* v, const void* out, c
 
 bool decode_sizes_ok(int B, int H, int splits) { return (long long)B * H * splits <= INT_MAX; }
 
+int decode_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv, int Nk,
+                int d, float scale, int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = check_common(q, k, v, out, lse, B, H, 1, Nk, scale, 0);
+  if (rc != ATTN_OK) return rc;
+  if (Hkv < 1 || H % Hkv != 0) return ATTN_E_INVALID;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (num_splits < 1 || num_splits > 256 || num_splits > Nk) return ATTN_E_INVALID;
+  if (!decode_sizes_ok(B, H, num_splits)) return ATTN_E_INVALID;
+  const size_t need = attn::decode_workspace_bytes(B, H, d, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ATTN_E_WORKSPACE;
+  return hip_status(attn::launch_decode(q, k, v, out, lse, B, H, Hkv, Nk, d, scale, dtype == ATTN_BF16, num_splits,
+                                        workspace, static_cast<hipStream_t>(stream)));
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv, int Nq, int Nk,
+             int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(q, k, v, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (Hkv < 1 || H % Hkv != 0) return ATTN_E_INVALID;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (Nq == 1) {
+    const int splits = attn::decode_default_splits(B, H, Nk, d);
+    return decode_impl(q, k, v, out, lse, B, H, Hkv, Nk, d, scale, dtype, splits, workspace, workspace_bytes, stream);
+  }
+  if (!prefill_head_ok(Nq, Nk, d)) return ATTN_E_INVALID;
+  const attn::SeqShape sh{nullptr, nullptr, H, H / Hkv, Nq, Nk};
+  return hip_status(attn::launch_prefill(q, k, v, out, lse, sh, B, Nq, d, scale, causal != 0, dtype == ATTN_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,31 +97,37 @@ size_t attn_fwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) 
 
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nk, int d,
                     float scale, int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(q, k, v, out, lse, B, H, 1, Nk, scale, 0);
-  if (rc != ATTN_OK) return rc;
-  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
-  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
-  if (num_splits < 1 || num_splits > 256 || num_splits > Nk) return ATTN_E_INVALID;
-  if (!decode_sizes_ok(B, H, num_splits)) return ATTN_E_INVALID;
-  const size_t need = attn::decode_workspace_bytes(B, H, d, num_splits);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ATTN_E_WORKSPACE;
-  return hip_status(attn::launch_decode(q, k, v, out, lse, B, H, Nk, d, scale, dtype == ATTN_BF16, num_splits,
-                                        workspace, static_cast<hipStream_t>(stream)));
+  return decode_impl(q, k, v, out, lse, B, H, H, Nk, d, scale, dtype, num_splits, workspace, workspace_bytes, stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq, int Nk, int d,
              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(q, k, v, out, lse, B, H, Nq, Nk, scale, causal);
-  if (rc != ATTN_OK) return rc;
+  return fwd_impl(q, k, v, out, lse, B, H, H, Nq, Nk, d, scale, causal, dtype, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv, int Nq,
+                 int Nk, int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return fwd_impl(q, k, v, out, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int nseq, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                    int H, int Hkv, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_E_INVALID;
+  if ((lse && !aligned4(lse)) || !aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return ATTN_E_INVALID;
+  if (nseq < 1 || H < 1 || Hkv < 1 || H % Hkv != 0) return ATTN_E_INVALID;
+  if (max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return ATTN_E_INVALID;
+  if (!good_scale(scale)) return ATTN_E_INVALID;
   if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
-  if (Nq == 1) {
-    const int splits = attn::decode_default_splits(B, H, Nk, d);
-    return attn_fwd_decode(q, k, v, out, lse, B, H, Nk, d, scale, dtype, splits, workspace, workspace_bytes, stream);
-  }
-  if (!prefill_head_ok(Nq, Nk, d)) return ATTN_E_INVALID;
-  return hip_status(attn::launch_prefill(q, k, v, out, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype == ATTN_BF16,
-                                         static_cast<hipStream_t>(stream)));
+  if (!prefill_head_ok(max_seqlen_q, max_seqlen_k, d) || !prefill_grid_ok(nseq, H, max_seqlen_q))
+    return ATTN_E_INVALID;
+  if (max_seqlen_q == 0 || total_q == 0) return ATTN_OK;  // no query: nothing to write
+  const attn::SeqShape sh{cu_seqlens_q, cu_seqlens_k, H, H / Hkv, total_q, total_k};
+  return hip_status(attn::launch_prefill(q, k, v, out, lse, sh, nseq, max_seqlen_q, d, scale, causal != 0,
+                                         dtype == ATTN_BF16, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {

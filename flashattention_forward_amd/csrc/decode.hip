@@ -67,7 +67,7 @@ __device__ __forceinline__ void widen8(u32x4 u, bool bf16, float* f) {
 template <int D, bool BF16>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    float* __restrict__ Opart, float* __restrict__ Lpart, int Nk, float c, int splits) {
+    float* __restrict__ Opart, float* __restrict__ Lpart, int Nk, float c, int splits, int H, int group) {
   constexpr int LPR = D / 8;            // lanes per K/V row
   constexpr int RPW = 64 / LPR;         // rows per wave load
   constexpr int NW = kDecThreads / 64;  // waves
@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
   const int s0 = (int)(((long)split * Nk) / splits), s1 = (int)(((long)(split + 1) * Nk) / splits);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = lane / LPR, ch = lane % LPR;
-  const size_t kbase = (size_t)bh * Nk * D;
+  // query head bh % H of batch bh / H reads K/V head (bh % H) / group
+  const size_t kbase = ((size_t)(bh / H) * (H / group) + (bh % H) / group) * Nk * D;
 
   float q[8];
   widen8(reinterpret_cast<const u32x4*>(Q + (size_t)bh * D)[ch], BF16, q);
@@ -181,12 +182,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 
 template <int D, bool BF16>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                           int Nk, float scale, int splits, void* workspace, hipStream_t stream) {
+                           int Hkv, int Nk, float scale, int splits, void* workspace, hipStream_t stream) {
   float* opart = static_cast<float*>(workspace);
   float* lpart = opart + (size_t)B * H * splits * D;
   hipLaunchKernelGGL((decode_partial_kernel<D, BF16>), dim3(B * H * splits), dim3(kDecThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits);
+                     static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits, H, H / Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, BF16>), dim3(B * H), dim3(D), 0, stream, opart, lpart,
@@ -209,13 +210,16 @@ int decode_default_splits(int B, int H, int Nk, int d) {
   return s;
 }
 
-hipError_t launch_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                         int Nk, int d, float scale, bool bf16, int splits, void* workspace,
-                         hipStream_t stream) {
-  if (d == 128 && bf16) return launch_decode_t<128, true>(q, k, v, out, lse, B, H, Nk, scale, splits, workspace, stream);
-  if (d == 128 && !bf16) return launch_decode_t<128, false>(q, k, v, out, lse, B, H, Nk, scale, splits, workspace, stream);
-  if (d == 64 && bf16) return launch_decode_t<64, true>(q, k, v, out, lse, B, H, Nk, scale, splits, workspace, stream);
-  if (d == 64 && !bf16) return launch_decode_t<64, false>(q, k, v, out, lse, B, H, Nk, scale, splits, workspace, stream);
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
+                         int Nk, int d, float scale, bool bf16, int splits, void* workspace, hipStream_t stream) {
+  if (d == 128 && bf16)
+    return launch_decode_t<128, true>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+  if (d == 128 && !bf16)
+    return launch_decode_t<128, false>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+  if (d == 64 && bf16)
+    return launch_decode_t<64, true>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+  if (d == 64 && !bf16)
+    return launch_decode_t<64, false>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
   return hipErrorInvalidValue;
 }
 

@@ -105,7 +105,7 @@ __device__ __forceinline__ void tile_load_lds(const __amdgpu_buffer_rsrc_t& r, c
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, float c, int nqb, int total, int paired) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, SeqShape sh, float c, int nqb, int total, int paired) {
   using C = PrefillCfg<D>;
   using M = Mfma<BF16>;
   typedef typename M::op8 op8;
@@ -129,13 +129,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   const int bh = logical / per_head;
   const int j_item = logical - bh * per_head;
   const int nitems = (paired && nqb - 1 - j_item != j_item) ? 2 : 1;
+  // this (sequence, head)'s rows; Nq and Nk are its own lengths from here on
+  const SeqSpan sp = seq_span(sh, bh / sh.H, bh % sh.H);
+  const int Nq = sp.nq, Nk = sp.nk;
   const int off = Nk - Nq;        // bottom-right causal alignment
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w >> 2, wg = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
-  const size_t qbase = (size_t)bh * Nq * D;
-  const size_t kbase = (size_t)bh * Nk * D;
+  const size_t qbase = sp.q_row0 * D;
+  const size_t kbase = sp.k_row0 * D;
   const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
   const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
   const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   for (int item = 0; item < nitems; ++item) {
     const int qb = paired ? (item == 0 ? nqb - 1 - j_item : j_item) : (CAUSAL ? nqb - 1 - j_item : j_item);
     const int q0 = qb * C::BM;
+    if (q0 >= Nq) continue;  // past a short packed sequence (uniform over the workgroup)
     // B operand of S^T = K Q^T: lane holds Q[qrow][16kk + 8h .. +7]; rows past Nq read as 0
     const int qmin_w = q0 + 128 * grp + 32 * wg;  // smallest query row of this wave
     const int qrow = qmin_w + l32;
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
 
     int kv_end = Nk;
     if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
-    const int T = (kv_end + C::BN - 1) / C::BN;
+    const int T = max(0, (kv_end + C::BN - 1) / C::BN);  // 0: no key visible to the block
 
     f32x16 o[C::MB_O];
 #pragma unroll
@@ -370,8 +374,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     }
 
     // ---- epilogue: combine the half-wave row sums, normalise, write O and LSE
+    // a row that saw no key (packed batches only) has l = 0: O = 0, LSE = -inf
     const float l_tot = pair_sum(l_run);
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < Nq) {
       uint16_t* dst = O + qbase + (size_t)qrow * D;
 #pragma unroll
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
           u[1] = __builtin_bit_cast(uint32_t, x1);
           *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g + 4 * h) = u;
         }
-      if (LSE != nullptr && h == 0) LSE[(size_t)bh * Nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+      if (LSE != nullptr && h == 0) LSE[sp.q_row0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
     }
   }  // work items
 }
@@ -400,26 +405,29 @@ static int device_cu_count() {
 }
 
 template <int D, bool BF16, bool CAUSAL>
-static hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                           int Nq, int Nk, float scale, hipStream_t stream) {
+static hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse, const SeqShape& sh,
+                           int nseq, int max_nq, float scale, hipStream_t stream) {
   using C = PrefillCfg<D>;
-  const int nqb = (Nq + C::BM - 1) / C::BM;
+  const int nqb = (max_nq + C::BM - 1) / C::BM;
   // pair causal blocks when the paired grid still fills every CU several times
-  // over (otherwise the last round of workgroups would run on few CUs)
-  const long pairs = (long)((nqb + 1) / 2) * B * H;
-  const int paired = (CAUSAL && pairs >= 4L * device_cu_count()) ? 1 : 0;
-  const int total = (paired ? (nqb + 1) / 2 : nqb) * B * H;
+  // over (otherwise the last round of workgroups would run on few CUs); packed
+  // batches have blocks of unequal length and are never paired
+  const long pairs = (long)((nqb + 1) / 2) * nseq * sh.H;
+  const int paired = (CAUSAL && sh.cu_q == nullptr && pairs >= 4L * device_cu_count()) ? 1 : 0;
+  const int total = (paired ? (nqb + 1) / 2 : nqb) * nseq * sh.H;
+  if (total == 0) return hipSuccess;
   hipLaunchKernelGGL((prefill_kernel<D, BF16, CAUSAL>), dim3(total), dim3(C::NT), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, Nq, Nk,
-                     scale * kLog2e, nqb, total, paired);
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, sh, scale * kLog2e, nqb,
+                     total, paired);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                          int Nq, int Nk, int d, float scale, bool causal, bool bf16, hipStream_t stream) {
-#define ATTN_DISPATCH(D_, BF_, CA_) \
-  if (d == D_ && bf16 == BF_ && causal == CA_) return launch_t<D_, BF_, CA_>(q, k, v, out, lse, B, H, Nq, Nk, scale, stream);
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* out, float* lse, const SeqShape& sh,
+                          int nseq, int max_nq, int d, float scale, bool causal, bool bf16, hipStream_t stream) {
+#define ATTN_DISPATCH(D_, BF_, CA_)          \
+  if (d == D_ && bf16 == BF_ && causal == CA_) \
+    return launch_t<D_, BF_, CA_>(q, k, v, out, lse, sh, nseq, max_nq, scale, stream);
   ATTN_DISPATCH(128, true, false)
   ATTN_DISPATCH(128, true, true)
   ATTN_DISPATCH(128, false, false)

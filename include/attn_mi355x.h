@@ -91,6 +91,45 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Grouped-query attention (GQA; MQA with Hkv = 1), one of the features the
+ * linux-konsole.com post "FlashAttention 4: fast, memory-efficient attention
+ * for LLMs" lists as missing from FA4: H query heads share Hkv key/value
+ * heads, and query head h attends with K/V head h / (H / Hkv) (consecutive
+ * query heads share one K/V head).  H must be a multiple of Hkv.
+ *   q, out [B,H,Nq,d]; k, v [B,Hkv,Nk,d]; lse [B,H,Nq].
+ * Everything else (dtype, d, causal, workspace for Nq == 1, errors) is as
+ * for attn_fwd, which is this call with Hkv = H.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length batch ("varlen" in the same post's list): nseq
+ * sequences of different lengths stored back to back along the token axis,
+ * head-major:
+ *   q, out [H, total_q, d]; k, v [Hkv, total_k, d]; lse [H, total_q] (may be NULL)
+ *   cu_seqlens_q, cu_seqlens_k: DEVICE int32 arrays of nseq + 1 offsets,
+ *   0 = cu[0] <= cu[1] <= ... <= cu[nseq] = total; sequence s owns query
+ *   tokens cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and key tokens
+ *   cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1.
+ *   max_seqlen_q, max_seqlen_k: upper bounds of the per-sequence lengths
+ *   (the grid covers max_seqlen_q queries per sequence; rows past it in a
+ *   longer sequence are not written).
+ * Each sequence is plain attention of its queries over its keys (GQA head
+ * mapping as in attn_fwd_gqa); causal masks are bottom-right aligned within
+ * each sequence.  A query row that sees no key (an empty key range, or
+ * causal with more queries than keys in its sequence) gets out = 0 and
+ * lse = -inf.  The offsets live in device memory and cannot be checked on
+ * the host: the kernel clamps them into [0, total] so malformed offsets
+ * address only rows of the right head.  No workspace.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq, int max_seqlen_q,
+                    int max_seqlen_k, int total_q, int total_k, int H, int Hkv, int d, float scale,
+                    int causal, int dtype, void* stream);
+
 /* Split count attn_fwd() uses for a decode problem (Nq == 1). */
 int attn_fwd_decode_splits(int B, int H, int Nk, int d);
 

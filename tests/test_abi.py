@@ -140,6 +140,26 @@ def test_bwd_workspace_size():
     assert L.attn_bwd_workspace_bytes(0, 1, 1, 1, 64, 0) == 0
 
 
+def test_gqa_and_varlen_reject():
+    L = Bd.lib()
+    gqa = lambda **kw: L.attn_fwd_gqa(A, A, A, A, A, 1, kw.get("H", 8), kw.get("Hkv", 2), kw.get("Nq", 16), 16,
+                                      kw.get("d", 128), 0.1, 0, 0, None, 0, None)
+    assert gqa(Hkv=3) == Bd.ATTN_E_INVALID          # H not a multiple of Hkv
+    assert gqa(Hkv=0) == Bd.ATTN_E_INVALID
+    assert gqa(d=80) == Bd.ATTN_E_UNSUPPORTED
+    assert gqa(Nq=1) == Bd.ATTN_E_WORKSPACE           # decode needs its workspace
+    vl = lambda **kw: L.attn_fwd_varlen(A, A, A, A, A, kw.get("cq", A), kw.get("ck", A), kw.get("nseq", 3),
+                                        kw.get("mq", 100), kw.get("mk", 100), 300, 300, kw.get("H", 4),
+                                        kw.get("Hkv", 2), kw.get("d", 64), kw.get("scale", 0.1), 0, 0, None)
+    assert vl(cq=None) == Bd.ATTN_E_INVALID and vl(ck=None) == Bd.ATTN_E_INVALID
+    assert vl(cq=A + 2) == Bd.ATTN_E_INVALID
+    assert vl(nseq=0) == Bd.ATTN_E_INVALID and vl(Hkv=3) == Bd.ATTN_E_INVALID
+    assert vl(mq=-1) == Bd.ATTN_E_INVALID and vl(scale=0.0) == Bd.ATTN_E_INVALID
+    assert vl(mk=2 ** 25) == Bd.ATTN_E_INVALID       # one sequence's keys past 2^32 bytes
+    assert vl(d=96) == Bd.ATTN_E_UNSUPPORTED
+    assert vl(mq=0) == Bd.ATTN_OK                      # no query: nothing launched
+
+
 def test_status_strings_and_build_info():
     for c in (0, -1, -2, -3, -4):
         assert Bd.status_str(c) and Bd.status_str(c) != "unknown status"
