@@ -16,8 +16,10 @@ Printed as ONE JSON line, which also carries
     workload on this host's cores;
   * other_workloads: the long causal fp16 sequence, the backward pass at the
     prefill configuration (algorithmic FLOPs of its five matrix products,
-    2.5x the forward's), the split-KV decode (GB/s over the K+V bytes) and the
-    quantised forward, each timed the same way (informational).
+    2.5x the forward's), grouped-query prefill and decode (32 query heads on
+    8 K/V heads), a packed variable-length causal batch, the split-KV decode
+    (GB/s over the K+V bytes) and the quantised forward, each timed the same
+    way (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
                        [--copy-calibration]
@@ -285,6 +287,57 @@ def main():
                 "frac_peak": round(fl / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": fl}
             del o, l
         del tq, tk, tv, tdo, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        # grouped-query prefill: 32 query heads on 8 K/V heads, causal
+        wg = G.WORKLOADS["gqa_4k_causal"]
+        tq = G.to_torch(G.draw_tensor(wg, "q", threads=16), "bf16")
+        wgk = G.shrink(wg, H=8)
+        tk, tv = (G.to_torch(G.draw_tensor(wgk, t, threads=16), "bf16") for t in ("k", "v"))
+        o = torch.empty_like(tq)
+        l = torch.empty((wg.B, wg.H, wg.Nq), device="cuda")
+        _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, causal=True, scale=wg.scale, out=o, lse=l)],
+                                args.steps, args.warmup)
+        other["gqa_4k_causal"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(wg.flops() / per[0] / 1e12, 3),
+                                  "frac_peak": round(wg.flops() / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                  "heads": "32 query / 8 K/V"}
+        del tq, tk, tv, o, l
+        # packed variable-length batch: 16 sequences of seeded lengths in [128, 4096],
+        # 32 query heads on 8 K/V heads, causal; FLOPs over the visible pairs
+        lens = np.random.default_rng([0, 7]).integers(128, 4097, 16)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+        tot = int(lens.sum())
+        wv = G.Workload("varlen_mix", 7, 1, 32, tot, tot, 128, "bf16", 1.0, True, 128 ** -0.5)
+        tq = G.to_torch(G.draw_tensor(wv, "q", threads=16)[0], "bf16")
+        wvk = G.shrink(wv, H=8)
+        tk, tv = (G.to_torch(G.draw_tensor(wvk, t, threads=16)[0], "bf16") for t in ("k", "v"))
+        o = torch.empty_like(tq)
+        l = torch.empty((32, tot), device="cuda")
+        mx = int(lens.max())
+        _, per = timed_launches([lambda: F.attn_fwd_varlen(tq, tk, tv, cu, cu, mx, mx, causal=True, scale=wv.scale,
+                                                           out=o, lse=l)], args.steps, args.warmup)
+        fl = float(sum(2.0 * 32 * n * n * 128 for n in lens))
+        other["varlen_mix_causal"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(fl / per[0] / 1e12, 3),
+                                      "frac_peak": round(fl / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                      "tokens": tot, "sequences": 16, "flops": fl}
+        del tq, tk, tv, o, l, cu
+        torch.cuda.empty_cache()
+        # grouped-query decode: 32 query heads on 8 K/V heads; GB/s over the K/V bytes
+        # that must be read once (the 8 K/V heads)
+        wgd = G.WORKLOADS["gqa_decode_8k"]
+        tq = G.to_torch(G.draw_tensor(wgd, "q", threads=16), "bf16")
+        wgdk = G.shrink(wgd, H=8)
+        tk, tv = (G.to_torch(G.draw_tensor(wgdk, t, threads=16), "bf16") for t in ("k", "v"))
+        o = torch.empty_like(tq)
+        l = torch.empty((wgd.B, wgd.H, 1), device="cuda")
+        ws = torch.empty(F.workspace_bytes(wgd.B, wgd.H, 1, wgd.Nk, wgd.d, 0, Hkv=8), device="cuda",
+                         dtype=torch.uint8)
+        _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, scale=wgd.scale, out=o, lse=l, workspace=ws)],
+                                args.steps, args.warmup)
+        kvb = 2 * wgd.B * 8 * wgd.Nk * wgd.d * 2
+        other["gqa_decode_8k"] = {"ms": round(per[0] * 1e3, 4), "gbs_kv": round(kvb / per[0] / 1e9, 1),
+                                  "frac_hbm_peak": round(kvb / per[0] / 1e9 / PEAK_HBM_GBS, 4), "kv_bytes": kvb,
+                                  "heads": "32 query / 8 K/V"}
+        del tq, tk, tv, o, l, ws
         torch.cuda.empty_cache()
         # split-KV decode
         wd = G.WORKLOADS["decode_8k"]

@@ -22,6 +22,7 @@ _P, _I, _L, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_floa
 SIGNATURES = {
     "attn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_fwd_gqa_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_fwd_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_fwd_decode_splits": (_I, [_I, _I, _I, _I]),
@@ -99,8 +100,11 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
-def workspace_bytes(B, H, Nq, Nk, d, dtype_code) -> int:
-    return int(lib().attn_fwd_workspace_bytes(B, H, Nq, Nk, d, dtype_code))
+def workspace_bytes(B, H, Nq, Nk, d, dtype_code, Hkv=None) -> int:
+    """Workspace attn_fwd needs (nonzero only for Nq == 1); Hkv < H for grouped-query heads."""
+    if Hkv is None or Hkv == H:
+        return int(lib().attn_fwd_workspace_bytes(B, H, Nq, Nk, d, dtype_code))
+    return int(lib().attn_fwd_gqa_workspace_bytes(B, H, Hkv, Nq, Nk, d, dtype_code))
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -121,7 +125,7 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
-    wsb = workspace_bytes(B, H, Nq, Nk, d, code)
+    wsb = workspace_bytes(B, H, Nq, Nk, d, code, Hkv)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
     args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None]

@@ -65,7 +65,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
   if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
   if (Nq == 1) {
-    const int splits = attn::decode_default_splits(B, H, Nk, d);
+    const int splits = attn::decode_default_splits(B, H, Hkv, Nk, d);
     return decode_impl(q, k, v, out, lse, B, H, Hkv, Nk, d, scale, dtype, splits, workspace, workspace_bytes, stream);
   }
   if (!prefill_head_ok(Nq, Nk, d)) return ATTN_E_INVALID;
@@ -85,14 +85,21 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
 
 int attn_fwd_decode_splits(int B, int H, int Nk, int d) {
   if (B < 1 || H < 1 || Nk < 1) return 0;
-  return attn::decode_default_splits(B, H, Nk, d);
+  return attn::decode_default_splits(B, H, H, Nk, d);
+}
+
+size_t attn_fwd_gqa_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int dtype) {
+  if (Hkv < 1 || H < 1 || H % Hkv != 0) return 0;
+  if (B < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128) || (dtype != ATTN_BF16 && dtype != ATTN_FP16)) return 0;
+  if (Nq != 1) return 0;
+  return attn::decode_workspace_bytes(B, H, d, attn::decode_default_splits(B, H, Hkv, Nk, d));
 }
 
 size_t attn_fwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128) || (dtype != ATTN_BF16 && dtype != ATTN_FP16))
     return 0;
   if (Nq != 1) return 0;
-  return attn::decode_workspace_bytes(B, H, d, attn::decode_default_splits(B, H, Nk, d));
+  return attn::decode_workspace_bytes(B, H, d, attn::decode_default_splits(B, H, H, Nk, d));
 }
 
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nk, int d,

@@ -64,36 +64,49 @@ __device__ __forceinline__ void widen8(u32x4 u, bool bf16, float* f) {
   }
 }
 
-template <int D, bool BF16>
+// HG query heads that share one K/V head are served by one workgroup: every
+// K and V row is read and widened once and used for all HG queries, each with
+// its own online-softmax state (grouped-query attention raises the work per
+// byte read by HG).  HG = 1 is plain multi-head attention.
+template <int D, bool BF16, int HG>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ Opart, float* __restrict__ Lpart, int Nk, float c, int splits, int H, int group) {
   constexpr int LPR = D / 8;            // lanes per K/V row
   constexpr int RPW = 64 / LPR;         // rows per wave load
   constexpr int NW = kDecThreads / 64;  // waves
-  constexpr int NS = NW * RPW;          // partial states per workgroup
-  constexpr int KCW = RPW * kDecUnroll; // keys per wave step
+  constexpr int NS = NW * RPW;          // partial states per workgroup and head
+  constexpr int UNR = HG >= 4 ? kDecUnroll / 2 : kDecUnroll;  // row loads in flight (registers)
+  constexpr int KCW = RPW * UNR;        // keys per wave step
   __shared__ float st_m[NS], st_l[NS];
   __shared__ float st_o[NS][D];
 
-  const int bh = blockIdx.x / splits, split = blockIdx.x - bh * splits;
+  const int wgi = blockIdx.x / splits, split = blockIdx.x - wgi * splits;
   const int s0 = (int)(((long)split * Nk) / splits), s1 = (int)(((long)(split + 1) * Nk) / splits);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = lane / LPR, ch = lane % LPR;
-  // query head bh % H of batch bh / H reads K/V head (bh % H) / group
-  const size_t kbase = ((size_t)(bh / H) * (H / group) + (bh % H) / group) * Nk * D;
+  // query heads bh0 .. bh0 + HG-1 (one batch b, heads h0 ..) all read K/V head h0 / group
+  const int bh0 = wgi * HG;
+  const int b = bh0 / H, h0 = bh0 - b * H;
+  const size_t kbase = ((size_t)b * (H / group) + h0 / group) * Nk * D;
 
-  float q[8];
-  widen8(reinterpret_cast<const u32x4*>(Q + (size_t)bh * D)[ch], BF16, q);
-
-  float m = -INFINITY, l = 0.f, acc[8];
+  float q[HG][8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int g = 0; g < HG; ++g) widen8(reinterpret_cast<const u32x4*>(Q + (size_t)(bh0 + g) * D)[ch], BF16, q[g]);
+
+  float m[HG], l[HG], acc[HG][8];
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
+  }
 
   for (int base = s0 + w * KCW; base < s1; base += NW * KCW) {
-    u32x4 kr[kDecUnroll], vr[kDecUnroll];
+    u32x4 kr[UNR], vr[UNR];
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const int key = base + u * RPW + row;
       kr[u] = u32x4{0u, 0u, 0u, 0u};
       vr[u] = u32x4{0u, 0u, 0u, 0u};
@@ -102,59 +115,74 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
         vr[u] = reinterpret_cast<const u32x4*>(V + kbase + (size_t)key * D)[ch];
       }
     }
-    float s[kDecUnroll];
-    float mc = -INFINITY;
+    float s[HG][UNR];
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       float kf[8];
       widen8(kr[u], BF16, kf);
-      float d = 0.f;
+      const bool live = base + u * RPW + row < s1;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) d = fmaf(q[j], kf[j], d);
-      d = group_sum<LPR>(d);
-      const int key = base + u * RPW + row;
-      s[u] = key < s1 ? d * c : -INFINITY;
-      mc = fmaxf(mc, s[u]);
+      for (int g = 0; g < HG; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d = fmaf(q[g][j], kf[j], d);
+        d = group_sum<LPR>(d);
+        s[g][u] = live ? d * c : -INFINITY;
+      }
     }
-    const float mn = fmaxf(m, mc);
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mref);
-    l *= alpha;
+    float mref[HG];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-    m = mn;
+    for (int g = 0; g < HG; ++g) {
+      float mc = s[g][0];
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      const float p = __builtin_amdgcn_exp2f(s[u] - mref);
-      l += p;
+      for (int u = 1; u < UNR; ++u) mc = fmaxf(mc, s[g][u]);
+      const float mn = fmaxf(m[g], mc);
+      mref[g] = mn == -INFINITY ? 0.f : mn;
+      const float alpha = m[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[g] - mref[g]);
+      l[g] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[g][j] *= alpha;
+      m[g] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
       float vf[8];
       widen8(vr[u], BF16, vf);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(p, vf[j], acc[j]);
+      for (int g = 0; g < HG; ++g) {
+        const float p = __builtin_amdgcn_exp2f(s[g][u] - mref[g]);
+        l[g] += p;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(p, vf[j], acc[g][j]);
+      }
     }
   }
 
-  // merge the NS states of this workgroup
-  const int g = w * RPW + row;
-  if (ch == 0) {
-    st_m[g] = m;
-    st_l[g] = l;
-  }
+  // merge the NS states of this workgroup, one head at a time through LDS
+  const int st = w * RPW + row;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st_o[g][8 * ch + j] = acc[j];
-  __syncthreads();
-  if (tid < D) {
-    float M = -INFINITY;
-    for (int i = 0; i < NS; ++i) M = fmaxf(M, st_m[i]);
-    float L = 0.f, o = 0.f;
-    for (int i = 0; i < NS; ++i) {
-      const float wgt = st_m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st_m[i] - M);
-      L = fmaf(st_l[i], wgt, L);
-      o = fmaf(st_o[i][tid], wgt, o);
+  for (int g = 0; g < HG; ++g) {
+    if (ch == 0) {
+      st_m[st] = m[g];
+      st_l[st] = l[g];
     }
-    const size_t ps = (size_t)bh * splits + split;
-    Opart[ps * D + tid] = o / L;
-    if (tid == 0) Lpart[ps] = (M + __log2f(L)) * kLn2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st_o[st][8 * ch + j] = acc[g][j];
+    __syncthreads();
+    if (tid < D) {
+      float M = -INFINITY;
+      for (int i = 0; i < NS; ++i) M = fmaxf(M, st_m[i]);
+      float L = 0.f, o = 0.f;
+      for (int i = 0; i < NS; ++i) {
+        const float wgt = st_m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st_m[i] - M);
+        L = fmaf(st_l[i], wgt, L);
+        o = fmaf(st_o[i][tid], wgt, o);
+      }
+      const size_t ps = (size_t)(bh0 + g) * splits + split;
+      Opart[ps * D + tid] = o / L;
+      if (tid == 0) Lpart[ps] = (M + __log2f(L)) * kLn2;
+    }
+    if (g + 1 < HG) __syncthreads();  // the LDS states are rewritten for the next head
   }
 }
 
@@ -180,12 +208,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   if (LSE != nullptr && d == 0) LSE[bh] = lse;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, int HG>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                            int Hkv, int Nk, float scale, int splits, void* workspace, hipStream_t stream) {
   float* opart = static_cast<float*>(workspace);
   float* lpart = opart + (size_t)B * H * splits * D;
-  hipLaunchKernelGGL((decode_partial_kernel<D, BF16>), dim3(B * H * splits), dim3(kDecThreads), 0, stream,
+  hipLaunchKernelGGL((decode_partial_kernel<D, BF16, HG>), dim3(B * H / HG * splits), dim3(kDecThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits, H, H / Hkv);
   hipError_t e = hipGetLastError();
@@ -195,15 +223,36 @@ hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* ou
   return hipGetLastError();
 }
 
+// heads per workgroup: the largest of 8, 4, 2 that divides the group size
+template <int D, bool BF16>
+hipError_t launch_decode_g(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                           int Hkv, int Nk, float scale, int splits, void* workspace, hipStream_t stream) {
+  switch (decode_heads_per_workgroup(H, Hkv)) {
+    case 8: return launch_decode_t<D, BF16, 8>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+    case 4: return launch_decode_t<D, BF16, 4>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+    case 2: return launch_decode_t<D, BF16, 2>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+    default: return launch_decode_t<D, BF16, 1>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+  }
+}
+
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int H, int d, int splits) {
   return (size_t)B * H * splits * (d + 1) * sizeof(float);
 }
 
-int decode_default_splits(int B, int H, int Nk, int d) {
+int decode_heads_per_workgroup(int H, int Hkv) {
+  const int group = H / Hkv;
+  return group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+}
+
+int decode_default_splits(int B, int H, int Hkv, int Nk, int d) {
   (void)d;
-  // aim for about 8192 workgroups (32 per CU) with at least 128 keys each
+  // aim for about 8192 (query head, key range) streams with at least 128 keys
+  // each.  A grouped workgroup serves several heads of a range at once; counting
+  // streams per query head still measured best for it (splitting its key range
+  // further only added partial states to write and merge)
+  (void)Hkv;
   long bh = (long)B * H;
   int s = 1;
   while (bh * s < 8192 && s < 256 && (long)(s * 2) * 128 <= Nk) s *= 2;
@@ -213,13 +262,13 @@ int decode_default_splits(int B, int H, int Nk, int d) {
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
                          int Nk, int d, float scale, bool bf16, int splits, void* workspace, hipStream_t stream) {
   if (d == 128 && bf16)
-    return launch_decode_t<128, true>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+    return launch_decode_g<128, true>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
   if (d == 128 && !bf16)
-    return launch_decode_t<128, false>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+    return launch_decode_g<128, false>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
   if (d == 64 && bf16)
-    return launch_decode_t<64, true>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+    return launch_decode_g<64, true>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
   if (d == 64 && !bf16)
-    return launch_decode_t<64, false>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
+    return launch_decode_g<64, false>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
   return hipErrorInvalidValue;
 }
 

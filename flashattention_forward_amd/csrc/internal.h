@@ -53,7 +53,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* out
 // Split-KV decode (Nq == 1): partial kernel + merge kernel; query head h
 // reads K/V head h / (H / Hkv).
 size_t decode_workspace_bytes(int B, int H, int d, int splits);
-int decode_default_splits(int B, int H, int Nk, int d);
+int decode_heads_per_workgroup(int H, int Hkv);  // query heads one decode workgroup serves
+int decode_default_splits(int B, int H, int Hkv, int Nk, int d);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* out, float* lse,
                          int B, int H, int Hkv, int Nk, int d, float scale, bool bf16, int splits,
                          void* workspace, hipStream_t stream);

@@ -98,9 +98,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * heads, and query head h attends with K/V head h / (H / Hkv) (consecutive
  * query heads share one K/V head).  H must be a multiple of Hkv.
  *   q, out [B,H,Nq,d]; k, v [B,Hkv,Nk,d]; lse [B,H,Nq].
- * Everything else (dtype, d, causal, workspace for Nq == 1, errors) is as
- * for attn_fwd, which is this call with Hkv = H.
+ * Everything else (dtype, d, causal, errors) is as for attn_fwd, which is
+ * this call with Hkv = H.  Nq == 1 needs a workspace of
+ * attn_fwd_gqa_workspace_bytes() bytes.  The decode kernels serve up to 8
+ * query heads of a group per workgroup, reading each K/V row once for all
+ * of them.
  */
+size_t attn_fwd_gqa_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int dtype);
 int attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse,
                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);

@@ -148,6 +148,11 @@ def test_gqa_and_varlen_reject():
     assert gqa(Hkv=0) == Bd.ATTN_E_INVALID
     assert gqa(d=80) == Bd.ATTN_E_UNSUPPORTED
     assert gqa(Nq=1) == Bd.ATTN_E_WORKSPACE           # decode needs its workspace
+    assert L.attn_fwd_gqa_workspace_bytes(64, 32, 8, 1, 8192, 128, 0) == 64 * 32 * 4 * 129 * 4
+    assert L.attn_fwd_gqa_workspace_bytes(64, 32, 32, 1, 8192, 128, 0) == L.attn_fwd_workspace_bytes(
+        64, 32, 1, 8192, 128, 0)
+    assert L.attn_fwd_gqa_workspace_bytes(1, 6, 4, 1, 100, 128, 0) == 0      # H not a multiple of Hkv
+    assert L.attn_fwd_gqa_workspace_bytes(1, 8, 2, 5, 100, 128, 0) == 0      # prefill needs none
     vl = lambda **kw: L.attn_fwd_varlen(A, A, A, A, A, kw.get("cq", A), kw.get("ck", A), kw.get("nseq", 3),
                                         kw.get("mq", 100), kw.get("mk", 100), 300, 300, kw.get("H", 4),
                                         kw.get("Hkv", 2), kw.get("d", 64), kw.get("scale", 0.1), 0, 0, None)

@@ -38,7 +38,9 @@ def _check(o, l, O, L):
 
 GQA = [  # (B, H, Hkv, Nq, Nk)
     (2, 8, 2, 300, 300), (1, 4, 1, 77, 333), (1, 6, 3, 129, 129), (2, 4, 2, 2, 700), (1, 8, 1, 600, 600),
-    (3, 8, 2, 1, 1000),   # Nq = 1: the split-KV decode path
+    # Nq = 1: the split-KV decode path, whose workgroups serve 8, 4, 2 or 1 query
+    # heads of a group together (group 4, 8, 2, 3 and MQA with 16 heads)
+    (3, 8, 2, 1, 1000), (2, 16, 2, 1, 777), (2, 6, 3, 1, 300), (1, 6, 2, 1, 4099), (2, 16, 1, 1, 513),
 ]
 
 
