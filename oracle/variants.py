@@ -21,9 +21,17 @@ FA4's forward; it defines neither.  Readings (the plainest ones):
 Every function reduces to the pinned dense oracle by slicing and head
 mapping only; no arithmetic of its own.
 
+Gradients (the backward pass, [trading post] "Backward: recompute instead of
+store"): dQ per query head; dK, dV of a shared K/V head are the sums over the
+query heads that read it; in a packed batch each sequence is its own
+problem, and a query row that sees no key has O = 0 whatever its inputs, so
+it contributes no gradient.
+
 Parity status: pinned (GQA equals dense attention with K/V heads repeated
 explicitly and torch's CPU float64 scaled_dot_product_attention with
-enable_gqa; varlen equals one dense call per sequence; empty rows;
+enable_gqa; varlen equals one dense call per sequence; empty rows; GQA
+gradients against torch autograd through repeat_interleave; varlen
+gradients against one dense backward per sequence and finite differences;
 tests/test_oracle_variants.py).
 """
 from __future__ import annotations
@@ -103,4 +111,30 @@ def attention_backward_gqa(q, k, v, do, scale: float, causal: bool = False):
             dq[b, h] = a
             dk[b, g] += bk
             dv[b, g] += bv
+    return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, do, cu_q, cu_k, scale: float, causal: bool = False):
+    """Gradients of sum(dO * O) for attention_varlen: q, do [H, total_q, d],
+    k, v [Hkv, total_k, d]; returns (dQ, dK, dV) fp64 with those shapes."""
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    H, Hkv = q.shape[0], k.shape[0]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for s in range(len(cu_q) - 1):
+        qa, qb = int(cu_q[s]), int(cu_q[s + 1])
+        ka, kb = int(cu_k[s]), int(cu_k[s + 1])
+        Nq, Nk = qb - qa, kb - ka
+        if Nq == 0 or Nk == 0:
+            continue
+        # rows that see no key (causal, Nq > Nk) have a constant O = 0
+        first = Nq - Nk if (causal and Nq > Nk) else 0
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            a, bk, bv = BW.attention_backward_head(q[h, qa + first:qb], k[g, ka:kb], v[g, ka:kb],
+                                                   do[h, qa + first:qb], scale, causal)
+            dq[h, qa + first:qb] = a
+            dk[g, ka:kb] += bk
+            dv[g, ka:kb] += bv
     return dq, dk, dv

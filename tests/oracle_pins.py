@@ -515,5 +515,51 @@ def pin_gqa_backward_torch(bwd_gqa, tol=1e-12):
             assert np.max(np.abs(g - t.grad.numpy())) <= tol
 
 
+def pin_varlen_backward(bwd_varlen, fwd_varlen, h=1e-5, tol=2e-8):
+    """Packed-batch gradients: (a) equal one dense backward per sequence
+    (dQ per sequence, dK and dV of a shared head summed over its query
+    heads; rows that see no key get dQ = 0), checked against torch's CPU
+    float64 autograd of each sequence's plain expression with repeated K/V
+    heads; (b) central finite differences of sum(dO * O) through the packed
+    forward oracle (pinned above) on a tiny batch with an empty key range
+    and a causal sequence with more queries than keys."""
+    lq, lk = [3, 4, 0, 2], [3, 2, 2, 0]
+    cq, ck = _cu(lq), _cu(lk)
+    H, Hkv = 2, 1
+    q, k, v, do = _rand(H, cq[-1], 2), _rand(Hkv, ck[-1], 2), _rand(Hkv, ck[-1], 2), _rand(H, cq[-1], 2)
+    for causal in (False, True):
+        got = bwd_varlen(q, k, v, do, cq, ck, 0.9, causal)
+        want = [np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)]
+        for s in range(len(lq)):
+            if lq[s] == 0 or lk[s] == 0:
+                continue
+            tq = torch.tensor(q[:, cq[s]:cq[s + 1]], requires_grad=True)
+            tk = torch.tensor(k[:, ck[s]:ck[s + 1]], requires_grad=True)
+            tv = torch.tensor(v[:, ck[s]:ck[s + 1]], requires_grad=True)
+            kk, vv = torch.repeat_interleave(tk, H // Hkv, 0), torch.repeat_interleave(tv, H // Hkv, 0)
+            sc = (tq @ kk.transpose(-1, -2)) * 0.9
+            if causal:
+                vis = torch.arange(lk[s])[None, :] <= torch.arange(lq[s])[:, None] + (lk[s] - lq[s])
+                sc = sc.masked_fill(~vis, float("-inf"))
+            p = torch.nan_to_num(torch.softmax(sc, dim=-1))       # rows with no key: O = 0
+            (p @ vv).backward(torch.tensor(do[:, cq[s]:cq[s + 1]]))
+            want[0][:, cq[s]:cq[s + 1]] = tq.grad.numpy()
+            want[1][:, ck[s]:ck[s + 1]] += tk.grad.numpy()
+            want[2][:, ck[s]:ck[s + 1]] += tv.grad.numpy()
+        for g_, w_ in zip(got, want):
+            assert np.max(np.abs(g_ - w_)) <= 1e-12
+        for which, x in enumerate((q, k, v)):
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                ap, am = [q, k, v], [q, k, v]
+                ap[which], am[which] = xp, xm
+                lp = float(np.sum(do * fwd_varlen(*ap, cq, ck, 0.9, causal)[0]))
+                lm = float(np.sum(do * fwd_varlen(*am, cq, ck, 0.9, causal)[0]))
+                fd = (lp - lm) / (2 * h)
+                assert abs(fd - got[which][idx]) <= tol * max(1.0, abs(fd)), (causal, which, idx)
+
+
 GQA_PINS = [pin_gqa_repeat, pin_gqa_torch]
 VARLEN_PINS = [pin_varlen_per_sequence, pin_varlen_empty_rows]

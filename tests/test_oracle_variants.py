@@ -22,6 +22,20 @@ def test_gqa_backward_pin():
     P.pin_gqa_backward_torch(V.attention_backward_gqa)
 
 
+def test_varlen_backward_pin():
+    P.pin_varlen_backward(V.attention_backward_varlen, V.attention_varlen)
+
+
+def test_varlen_backward_mistake_is_caught():
+    """Gradients of the no-key rows left to the dense formula (NaN/garbage) or a
+    shared head's dK not summed over its query heads must fail the pin."""
+    def no_sum(q, k, v, do, cq, ck, s, c):
+        dq, dk, dv = V.attention_backward_varlen(q, k, v, do, cq, ck, s, c)
+        return dq, dk / 2.0, dv
+    with pytest.raises(AssertionError):
+        P.pin_varlen_backward(no_sum, V.attention_varlen)
+
+
 def test_kv_head_rejects_uneven_groups():
     with pytest.raises(ValueError):
         V.kv_head(0, 6, 4)
