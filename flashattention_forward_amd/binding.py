@@ -30,6 +30,9 @@ SIGNATURES = {
     "attn_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
     "attn_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_bwd_gqa": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                             _P, _Z, _P]),
     "attn_quantize_rows_i8": (_I, [_P, _P, _P, _L, _I, _P]),
     "attn_quantize_e4m3_workspace_bytes": (_Z, [_L]),
     "attn_quantize_tensor_e4m3": (_I, [_P, _P, _P, _L, _P, _Z, _P]),
@@ -168,12 +171,13 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
 
 def attn_bwd(q, k, v, out, dout, lse, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
              workspace=None):
-    """dQ, dK, dV of sum(dout * out) for out, lse = attn_fwd(q, k, v, causal, scale)."""
+    """dQ, dK, dV of sum(dout * out) for out, lse = attn_fwd(q, k, v, causal, scale).
+    k, v may have fewer heads than q (grouped-query attention)."""
     torch = _torch()
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or out.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("q, out, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != (B, Hkv, Nk, d) or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, out, dout must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
     if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
         raise ValueError("q, k, v, out, dout must share one dtype")
     if lse is None or lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
@@ -186,10 +190,40 @@ def attn_bwd(q, k, v, out, dout, lse, causal: bool = False, scale: float | None 
     wsb = int(lib().attn_bwd_workspace_bytes(B, H, Nq, Nk, d, code))
     if workspace is None:
         workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
-    rc = lib().attn_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
-                        _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, H, Nq, Nk, d, scale,
-                        int(bool(causal)), code, _dev(workspace, "workspace"), workspace.numel(), _stream())
-    _check(rc, "attn_bwd")
+    args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"), _dev(lse, "lse"),
+            _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv")]
+    tail = [d, scale, int(bool(causal)), code, _dev(workspace, "workspace"), workspace.numel(), _stream()]
+    if Hkv == H:
+        _check(lib().attn_bwd(*args, B, H, Nq, Nk, *tail), "attn_bwd")
+    else:
+        _check(lib().attn_bwd_gqa(*args, B, H, Hkv, Nq, Nk, *tail), "attn_bwd_gqa")
+    return dq, dk, dv
+
+
+def attn_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients for attn_fwd_varlen (same packed layouts)."""
+    torch = _torch()
+    H, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    if k.shape != (Hkv, total_k, d) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, out, dout must be [H, total_q, d] and k, v [Hkv, total_k, d]")
+    if lse is None or lse.shape != (H, total_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be the [H, total_q] float32 log-sum-exp of attn_fwd_varlen")
+    nseq = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(16, H * total_q * 8), device=q.device, dtype=torch.uint8)
+    rc = lib().attn_bwd_varlen(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
+                               _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"),
+                               _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), nseq,
+                               int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, H, Hkv, d, scale,
+                               int(bool(causal)), _dtype_code(q), _dev(workspace, "workspace"), workspace.numel(),
+                               _stream())
+    _check(rc, "attn_bwd_varlen")
     return dq, dk, dv
 
 

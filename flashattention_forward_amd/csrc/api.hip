@@ -142,24 +142,61 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) 
   (void)d;
   (void)dtype;
   if (B < 1 || H < 1 || Nq < 1) return 0;
-  return attn::bwd_workspace_bytes(B, H, Nq);
+  return attn::bwd_workspace_bytes((long)B * H * Nq);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
              void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
              void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd_gqa(q, k, v, out, dout, lse, dq, dk, dv, B, H, H, Nq, Nk, d, scale, causal, dtype, workspace,
+                      workspace_bytes, stream);
+}
+
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common(q, k, v, out, lse, B, H, Nq, Nk, scale, causal);
   if (rc != ATTN_OK) return rc;
+  if (Hkv < 1 || H % Hkv != 0) return ATTN_E_INVALID;
   if (!dout || !lse || !dq || !dk || !dv) return ATTN_E_INVALID;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_E_INVALID;
   if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
   if (!prefill_head_ok(Nq, Nk, d) || !prefill_grid_ok(B, H, Nk)) return ATTN_E_INVALID;
   if ((long long)Nq * 8 > (long long)UINT32_MAX) return ATTN_E_INVALID;
-  if (!workspace || workspace_bytes < attn::bwd_workspace_bytes(B, H, Nq) || !aligned16(workspace))
+  const long rows = (long)B * H * Nq;
+  if (!workspace || workspace_bytes < attn::bwd_workspace_bytes(rows) || !aligned16(workspace))
     return ATTN_E_WORKSPACE;
-  return hip_status(attn::launch_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal != 0,
-                                     dtype == ATTN_BF16, workspace, static_cast<hipStream_t>(stream)));
+  const attn::SeqShape sh{nullptr, nullptr, H, H / Hkv, Nq, Nk};
+  return hip_status(attn::launch_bwd(q, k, v, out, dout, lse, dq, dk, dv, sh, B, Nq, Nk, rows, d, scale,
+                                     causal != 0, dtype == ATTN_BF16, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                    int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int H, int Hkv, int d, float scale,
+                    int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+    return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned4(lse) || !aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k))
+    return ATTN_E_INVALID;
+  if (nseq < 1 || H < 1 || Hkv < 1 || H % Hkv != 0) return ATTN_E_INVALID;
+  if (max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0) return ATTN_E_INVALID;
+  if (!good_scale(scale)) return ATTN_E_INVALID;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (!prefill_head_ok(max_seqlen_q, max_seqlen_k, d) || !prefill_grid_ok(nseq, H, max_seqlen_q) ||
+      !prefill_grid_ok(nseq, H, max_seqlen_k) || (long long)max_seqlen_q * 8 > (long long)UINT32_MAX)
+    return ATTN_E_INVALID;
+  const long rows = (long)H * total_q;
+  if (!workspace || workspace_bytes < attn::bwd_workspace_bytes(rows) || !aligned16(workspace))
+    return ATTN_E_WORKSPACE;
+  if (total_q == 0 && total_k == 0) return ATTN_OK;  // nothing to differentiate
+  const attn::SeqShape sh{cu_seqlens_q, cu_seqlens_k, H, H / Hkv, total_q, total_k};
+  return hip_status(attn::launch_bwd(q, k, v, out, dout, lse, dq, dk, dv, sh, nseq, max_seqlen_q, max_seqlen_k,
+                                     rows, d, scale, causal != 0, dtype == ATTN_BF16, workspace,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int attn_quantize_rows_i8(const void* x, int8_t* x8, float* scales, long rows, int d, void* stream) {

@@ -122,7 +122,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && part == 0) LD[row] = make_float2(LSE[row] * kLog2e, acc);
+  // a row that saw no key (LSE = -inf, packed batches) gets +inf, so every
+  // probability rebuilt for it is exp2(-inf) = 0 and it adds no gradient
+  if (row < rows && part == 0) {
+    const float lse = LSE[row];
+    LD[row] = make_float2(lse == -INFINITY ? INFINITY : lse * kLog2e, acc);
+  }
 }
 
 // ---------------------------------------------------------------- bwd_kv
@@ -130,7 +135,7 @@ template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int Nq, int Nk, float c, float scale, int nkb, int total) {
+    uint16_t* __restrict__ dV, SeqShape sh, float c, float scale, int nkb, int total) {
   using C = BwdCfg<D>;
   using M = Mfma<BF16>;
   typedef typename M::op8 op8;
@@ -145,18 +150,24 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
   constexpr bool VLDS = D == 128;
   __shared__ __attribute__((aligned(1024))) char vws[VLDS ? C::NW * 32 * C::ROWB : 16];
 
+  // work item: 128 keys of one (sequence, K/V head); the group's query heads
+  // all read them, so dK and dV sum over the group's queries
   const int logical = xcd_remap(blockIdx.x, total);
-  const int bh = logical / nkb;
-  const int k0 = (logical - bh * nkb) * C::BO;
+  const int Hkv = sh.H / sh.group;
+  const int sk = logical / nkb;
+  const int k0 = (logical - sk * nkb) * C::BO;
+  const int sq = sk / Hkv, hk = sk - sq * Hkv;
+  const SeqSpan sp = seq_span(sh, sq, hk * sh.group);  // the group's first query head
+  const int Nq = sp.nq, Nk = sp.nk;
+  if (k0 >= Nk) return;  // past a short packed sequence (uniform over the workgroup)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int off = Nk - Nq;  // bottom-right causal alignment
-  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
-  const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
-  const auto rdo = make_rsrc(dO + qbase, (uint32_t)Nq * D * 2);
+  const size_t kbase = sp.k_row0 * D;
+  // query head gi of the group starts qstride rows after head gi-1
+  const size_t qstride = sh.cu_q != nullptr ? (size_t)sh.Nq : (size_t)Nq;
   const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
   const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
-  const auto rld = make_rsrc(LD + (size_t)bh * Nq, (uint32_t)Nq * 8);
 
   // this wave's keys: K and V rows as B operands (n = key, k = d)
   const int kw0 = k0 + 32 * w;
@@ -181,7 +192,12 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
     const int row = (C::LPW * w + i) * C::RPI + lane / C::SPR, ps = lane % C::SPR;
     goff[i] = (uint32_t)row * C::ROWB + 16 * (ps ^ bswz<D>(row));
   }
-  auto issue = [&](int st, char* qt, char* dt, char* lt) __attribute__((always_inline)) {
+  // Q, dO and (LSE, D) rows of query step st of the group's query head gi
+  auto issue = [&](int gi, int st, char* qt, char* dt, char* lt) __attribute__((always_inline)) {
+    const size_t qrow0 = sp.q_row0 + (size_t)gi * qstride;
+    const auto rq = make_rsrc(Q + qrow0 * D, (uint32_t)Nq * D * 2);
+    const auto rdo = make_rsrc(dO + qrow0 * D, (uint32_t)Nq * D * 2);
+    const auto rld = make_rsrc(LD + qrow0, (uint32_t)Nq * 8);
     const uint32_t base = (uint32_t)(st * C::BS) * C::ROWB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
@@ -328,17 +344,23 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // queries that see at least one of this workgroup's keys
+  // query steps that see at least one of this workgroup's keys, for every
+  // query head of the group in turn: step u is step s0 + u % nper of head u / nper
   int s0 = 0;
   if (CAUSAL) s0 = max(0, k0 - off) / C::BS;
   const int ns = (Nq + C::BS - 1) / C::BS;
-  issue(s0, q0s, d0s, l0s);
+  const int nper = max(0, ns - s0);
+  const int nu = sh.group * nper;
+  if (nu > 0) issue(0, s0, q0s, d0s, l0s);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int st = s0; st < ns; ++st) {
-    const bool odd = (st - s0) & 1;
-    if (st + 1 < ns) issue(st + 1, odd ? q0s : q1s, odd ? d0s : d1s, odd ? l0s : l1s);
-    step(st, odd ? q1s : q0s, odd ? d1s : d0s, odd ? l1s : l0s);
+  for (int u = 0; u < nu; ++u) {
+    const bool odd = u & 1;
+    if (u + 1 < nu) {
+      const int gn = (u + 1) / nper;
+      issue(gn, s0 + (u + 1 - gn * nper), odd ? q0s : q1s, odd ? d0s : d1s, odd ? l0s : l1s);
+    }
+    step(s0 + u % nper, odd ? q1s : q0s, odd ? d1s : d0s, odd ? l1s : l0s);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -363,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dQ, int Nq, int Nk,
+    const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dQ, SeqShape sh,
     float c, float scale, int nqb, int total) {
   using C = BwdCfg<D>;
   using M = Mfma<BF16>;
@@ -378,10 +400,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   int qb = logical - bh * nqb;
   if (CAUSAL) qb = nqb - 1 - qb;  // longest query blocks first
   const int q0 = qb * C::BO;
+  // this (sequence, query head)'s rows; its K/V head is head / group
+  const SeqSpan sp = seq_span(sh, bh / sh.H, bh % sh.H);
+  const int Nq = sp.nq, Nk = sp.nk;
+  if (q0 >= Nq) return;  // past a short packed sequence (uniform over the workgroup)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int off = Nk - Nq;
-  const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const size_t qbase = sp.q_row0 * D, kbase = sp.k_row0 * D;
   const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
   const auto rdo = make_rsrc(dO + qbase, (uint32_t)Nq * D * 2);
   const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
@@ -398,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
   float Lq = 0.f, Dq = 0.f;
   if (query < Nq) {
-    const float2 x = LD[(size_t)bh * Nq + query];
+    const float2 x = LD[sp.q_row0 + query];
     Lq = x.x;
     Dq = x.y;
   }
@@ -505,40 +531,42 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, float scale,
-                        void* workspace, hipStream_t stream) {
+                        const float* lse, void* dq, void* dk, void* dv, const SeqShape& sh, int nseq, int max_nq,
+                        int max_nk, long q_rows, float scale, void* workspace, hipStream_t stream) {
   using C = BwdCfg<D>;
   float2* ld = static_cast<float2*>(workspace);
-  const long rows = (long)B * H * Nq;
   constexpr int RPB = 256 / (D / 8);  // rows per bwd_pre block
-  hipLaunchKernelGGL((bwd_pre_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, ld, rows);
+  hipLaunchKernelGGL((bwd_pre_kernel<D, BF16>), dim3((unsigned)((q_rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, ld, q_rows);
   const float c = scale * kLog2e;
-  const int nkb = (Nk + C::BO - 1) / C::BO;
-  const int totk = nkb * B * H;
-  hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, CAUSAL>), dim3(totk), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
-                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), Nq, Nk, c, scale, nkb, totk);
-  const int nqb = (Nq + C::BO - 1) / C::BO;
-  const int totq = nqb * B * H;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL>), dim3(totq), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
-                     static_cast<uint16_t*>(dq), Nq, Nk, c, scale, nqb, totq);
+  const int nkb = (max_nk + C::BO - 1) / C::BO;
+  const int totk = nkb * nseq * (sh.H / sh.group);
+  if (totk > 0)
+    hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, CAUSAL>), dim3(totk), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk);
+  const int nqb = (max_nq + C::BO - 1) / C::BO;
+  const int totq = nqb * nseq * sh.H;
+  if (totq > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL>), dim3(totq), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
+                       static_cast<uint16_t*>(dq), sh, c, scale, nqb, totq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int H, int Nq) { return (size_t)B * H * Nq * sizeof(float2); }
+size_t bwd_workspace_bytes(long q_rows) { return (size_t)q_rows * sizeof(float2); }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                      void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, bool causal,
-                      bool bf16, void* workspace, hipStream_t stream) {
-#define ATTN_BWD(D_, BF_, CA_)                                                                                   \
-  if (d == D_ && bf16 == BF_ && causal == CA_)                                                                   \
-    return launch_bwd_t<D_, BF_, CA_>(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, scale, workspace, stream);
+                      void* dq, void* dk, void* dv, const SeqShape& sh, int nseq, int max_nq, int max_nk, long q_rows,
+                      int d, float scale, bool causal, bool bf16, void* workspace, hipStream_t stream) {
+#define ATTN_BWD(D_, BF_, CA_)                                                                                \
+  if (d == D_ && bf16 == BF_ && causal == CA_)                                                                \
+    return launch_bwd_t<D_, BF_, CA_>(q, k, v, out, dout, lse, dq, dk, dv, sh, nseq, max_nq, max_nk, q_rows,  \
+                                      scale, workspace, stream);
   ATTN_BWD(128, true, false)
   ATTN_BWD(128, true, true)
   ATTN_BWD(128, false, false)

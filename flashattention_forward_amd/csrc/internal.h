@@ -60,11 +60,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
                          void* workspace, hipStream_t stream);
 
 // Backward pass: preprocess (log-sum-exp in base 2, rowsum(dO * O)) into a
-// float2 [B, H, Nq] workspace, then the dK/dV and dQ kernels.
-size_t bwd_workspace_bytes(int B, int H, int Nq);
+// float2 workspace with one entry per query row (q_rows of them: B*H*Nq dense,
+// H*total_q packed), then the dK/dV and dQ kernels, over nseq sequences of at
+// most max_nq queries and max_nk keys (see SeqShape for the layouts).
+size_t bwd_workspace_bytes(long q_rows);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                      void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, bool causal,
-                      bool bf16, void* workspace, hipStream_t stream);
+                      void* dq, void* dk, void* dv, const SeqShape& sh, int nseq, int max_nq, int max_nk, long q_rows,
+                      int d, float scale, bool causal, bool bf16, void* workspace, hipStream_t stream);
 
 // Quantisation kernels and the quantised forward.
 hipError_t launch_quantize_rows_i8(const void* x, int8_t* x8, float* scales, long rows, int d,

@@ -182,6 +182,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of attn_fwd_gqa: q, out, dout, dq [B,H,Nq,d]; k, v, dk, dv
+ * [B,Hkv,Nk,d]; lse [B,H,Nq].  dK and dV of a shared K/V head are the sums of
+ * the contributions of all H/Hkv query heads that read it (computed inside
+ * one workgroup per key block, no atomics).  Workspace as attn_bwd
+ * (attn_bwd_workspace_bytes with the query head count H).
+ */
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk,
+                 int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Backward of attn_fwd_varlen (same packed layouts and offsets; dq like q,
+ * dk and dv like k and v; lse [H, total_q] as attn_fwd_varlen wrote it, so a
+ * row that saw no key carries -inf and gets dq = 0).  Every token row inside
+ * a sequence is written (a sequence with no keys gets dq = 0, one with no
+ * queries dk = dv = 0).  workspace: at least H * total_q * 8 bytes
+ * (attn_bwd_workspace_bytes(1, H, total_q, ...)), 16-byte aligned.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int nseq, int max_seqlen_q, int max_seqlen_k, int total_q,
+                    int total_k, int H, int Hkv, int d, float scale, int causal, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * Quantisation of bf16 inputs for the quantised forward (token-level INT8
  * post-training quantisation of Q and K as in the hoodcat.net post
  * "INT-FlashAttention: an INT8 quantisation architecture compatible with

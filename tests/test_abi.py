@@ -163,6 +163,15 @@ def test_gqa_and_varlen_reject():
     assert vl(mk=2 ** 25) == Bd.ATTN_E_INVALID       # one sequence's keys past 2^32 bytes
     assert vl(d=96) == Bd.ATTN_E_UNSUPPORTED
     assert vl(mq=0) == Bd.ATTN_OK                      # no query: nothing launched
+    bg = lambda **kw: L.attn_bwd_gqa(A, A, A, A, A, A, A, A, A, 1, kw.get("H", 8), kw.get("Hkv", 2), 16, 16, 128,
+                                     0.1, 0, 0, kw.get("ws", A), kw.get("wsb", 1 << 20), None)
+    assert bg(Hkv=3) == Bd.ATTN_E_INVALID and bg(ws=None) == Bd.ATTN_E_WORKSPACE
+    assert bg(wsb=8 * 16 * 8 - 1) == Bd.ATTN_E_WORKSPACE
+    bv = lambda **kw: L.attn_bwd_varlen(A, A, A, A, A, A, A, A, A, kw.get("cq", A), A, 2, 50, 50, 100, 100,
+                                        kw.get("H", 4), 2, 64, 0.1, 0, 0, kw.get("ws", A), kw.get("wsb", 1 << 20),
+                                        None)
+    assert bv(cq=None) == Bd.ATTN_E_INVALID and bv(H=3) == Bd.ATTN_E_INVALID
+    assert bv(wsb=4 * 100 * 8 - 1) == Bd.ATTN_E_WORKSPACE and bv(ws=MIS) == Bd.ATTN_E_WORKSPACE
 
 
 def test_status_strings_and_build_info():

@@ -127,3 +127,79 @@ def test_gqa_full_size_sampled(F):
         el = np.max(np.abs(from_dev(lse[b, h])[rows] - L))
         print(f"  head ({b},{h}) -> kv {g}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
         assert eo <= O_TOL and el <= LSE_TOL
+
+
+# ---------------------------------------------------------------- backward
+# Gate as for the dense backward: max |G - G_ref| <= GRAD_TOL * max |G_ref| per
+# gradient tensor (P and dS are rounded to 16 bits for the matrix cores).
+GRAD_TOL = 2e-2
+
+
+def _check_grads(got, ref):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.isfinite(g).all(), f"unwritten or non-finite {name}"
+        e, m = float(np.max(np.abs(g - r))), float(np.max(np.abs(r)))
+        print(f"  {name}: max err {e:.3e} (max |ref| {m:.3e})", flush=True)
+        assert e <= GRAD_TOL * m, (name, e, m)
+
+
+GQA_BWD = [(2, 8, 2, 300, 300), (1, 4, 1, 77, 333), (1, 6, 3, 129, 129), (1, 8, 4, 256, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", GQA_BWD, ids=lambda s: "x".join(map(str, s)))
+def test_gqa_backward(F, dtype, d, causal, shape):
+    import torch
+    from tests.gpu_util import from_dev, nan_like, to_dev
+    B, H, Hkv, Nq, Nk = shape
+    if causal and Nq > Nk:
+        pytest.skip("causal needs Nq <= Nk")
+    wq = G.Workload(f"gqa_bwd_{dtype}_{d}", 90 + d + (dtype == "fp16"), B, H, Nq, Nk, d, dtype, 1.0, causal,
+                    1 / math.sqrt(d))
+    wk = G.shrink(wq, H=Hkv)
+    q, do = G.draw_tensor(wq, "q"), G.draw_tensor(wq, "do")
+    k, v = G.draw_tensor(wk, "k"), G.draw_tensor(wk, "v")
+    tq, tk, tv, tdo = (to_dev(x, dtype) for x in (q, k, v, do))
+    print(f"  gpu: GQA bwd B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal}", flush=True)
+    out, lse = F.attn_fwd(tq, tk, tv, causal=causal, scale=wq.scale)
+    dq, dk, dv = nan_like(tq), nan_like(tk), nan_like(tv)
+    F.attn_bwd(tq, tk, tv, out, tdo, lse, causal=causal, scale=wq.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    f = lambda x: G.to_f64(x, dtype)
+    ref = V.attention_backward_gqa(f(q), f(k), f(v), f(do), wq.scale, causal)
+    _check_grads(tuple(from_dev(t) for t in (dq, dk, dv)), ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", range(len(VARLEN)))
+def test_varlen_backward(F, dtype, d, causal, case):
+    import torch
+    from tests.gpu_util import from_dev, nan_like, to_dev
+    lq, lk, H, Hkv = VARLEN[case]
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    tq_, tk_ = int(cq[-1]), int(ck[-1])
+    wq = G.Workload(f"varlen_bwd_{dtype}_{d}", 100 + d + (dtype == "fp16") + 2 * case, 1, H, tq_, tk_, d, dtype,
+                    1.0, causal, 1 / math.sqrt(d))
+    wk = G.shrink(wq, H=Hkv)
+    q, do = G.draw_tensor(wq, "q")[0], G.draw_tensor(wq, "do")[0]
+    k, v = G.draw_tensor(wk, "k")[0], G.draw_tensor(wk, "v")[0]
+    tq, tk, tv, tdo = (to_dev(x, dtype) for x in (q, k, v, do))
+    cu_q, cu_k = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    print(f"  gpu: varlen bwd lq={lq} lk={lk} H={H} Hkv={Hkv} d={d} {dtype} causal={causal}", flush=True)
+    out, lse = F.attn_fwd_varlen(tq, tk, tv, cu_q, cu_k, max(lq), max(lk), causal=causal, scale=wq.scale)
+    dq, dk, dv = nan_like(tq), nan_like(tk), nan_like(tv)
+    F.attn_bwd_varlen(tq, tk, tv, out, tdo, lse, cu_q, cu_k, max(lq), max(lk), causal=causal, scale=wq.scale,
+                      dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    f = lambda x: G.to_f64(x, dtype)
+    ref = V.attention_backward_varlen(f(q), f(k), f(v), f(do), cq, ck, wq.scale, causal)
+    got = tuple(from_dev(t) for t in (dq, dk, dv))
+    # rows that see no key: exactly zero gradient
+    _, L = V.attention_varlen(f(q), f(k), f(v), cq, ck, wq.scale, causal)
+    assert np.all(got[0][~np.isfinite(L)] == 0.0)
+    _check_grads(got, ref)
