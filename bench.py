@@ -52,7 +52,8 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4k_traffic.json")
 COPY_BYTES = 1 << 30          # bytes read (and written) by one calibration copy
 PREFILL_KERNEL = "prefill_kernel<128, true, false>"   # bf16, non-causal
-KERNEL_SOURCES = ["flashattention_forward_amd/csrc/prefill.hip", "flashattention_forward_amd/csrc/common.h"]
+KERNEL_SOURCES = ["flashattention_forward_amd/csrc/prefill.hip", "flashattention_forward_amd/csrc/common.h",
+                  "flashattention_forward_amd/csrc/internal.h"]
 
 
 def kernel_source_sha() -> str:
@@ -300,7 +301,17 @@ def main():
         other["gqa_4k_causal"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(wg.flops() / per[0] / 1e12, 3),
                                   "frac_peak": round(wg.flops() / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4),
                                   "heads": "32 query / 8 K/V"}
-        del tq, tk, tv, o, l
+        # its backward (dK, dV of a K/V head summed over its 4 query heads)
+        tdo = G.to_torch(G.draw_tensor(wg, "do", threads=16), "bf16")
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(wg.B * wg.H * wg.Nq * 8, device="cuda", dtype=torch.uint8)
+        _, per = timed_launches([lambda: F.attn_bwd(tq, tk, tv, o, tdo, l, causal=True, scale=wg.scale, dq=dq, dk=dk,
+                                                    dv=dv, workspace=ws)], max(5, args.steps // 2), args.warmup)
+        fl = 2.5 * wg.flops()
+        other["backward_gqa_4k_causal"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(fl / per[0] / 1e12, 3),
+                                           "frac_peak": round(fl / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                           "heads": "32 query / 8 K/V"}
+        del tq, tk, tv, o, l, tdo, dq, dk, dv, ws
         # packed variable-length batch: 16 sequences of seeded lengths in [128, 4096],
         # 32 query heads on 8 K/V heads, causal; FLOPs over the visible pairs
         lens = np.random.default_rng([0, 7]).integers(128, 4097, 16)
