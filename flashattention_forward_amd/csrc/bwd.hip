@@ -80,6 +80,21 @@ __device__ __forceinline__ uint16_t to_half_bits(float x) {
   return __builtin_bit_cast(uint32_t, p) & 0xffffu;
 }
 
+// Causal grids: the blocks of one head differ in work (a key block near the
+// start is seen by many queries, a query block near the end sees many keys).
+// Items are taken in chunks of `chunk` heads, block-major inside a chunk (rank
+// 0, the most work, of every head of the chunk first), and chunks stay
+// contiguous, so each XCD's contiguous range of items (xcd_remap) still covers
+// whole heads while the dispatcher starts the longest items first.
+__device__ __forceinline__ void heavy_first(int logical, int nblk, int nheads, int chunk, int& head, int& rank) {
+  const int c = logical / (nblk * chunk);
+  const int c0 = c * chunk;
+  const int ch = min(chunk, nheads - c0);
+  const int i = logical - c * nblk * chunk;
+  rank = i / ch;
+  head = c0 + (i - rank * ch);
+}
+
 // ---------------------------------------------------------------- bwd_pre
 // One row per D/8 lanes (16 bytes each): D_i = sum_c dO_ic O_ic in fp32 and
 // the log-sum-exp in base 2.
@@ -135,7 +150,7 @@ template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, SeqShape sh, float c, float scale, int nkb, int total) {
+    uint16_t* __restrict__ dV, SeqShape sh, float c, float scale, int nkb, int total, int chunk) {
   using C = BwdCfg<D>;
   using M = Mfma<BF16>;
   typedef typename M::op8 op8;
@@ -154,8 +169,14 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
   // all read them, so dK and dV sum over the group's queries
   const int logical = xcd_remap(blockIdx.x, total);
   const int Hkv = sh.H / sh.group;
-  const int sk = logical / nkb;
-  const int k0 = (logical - sk * nkb) * C::BO;
+  int sk, kb;
+  if (CAUSAL) {
+    heavy_first(logical, nkb, total / nkb, chunk, sk, kb);  // key block 0 has the most queries
+  } else {
+    sk = logical / nkb;
+    kb = logical - sk * nkb;
+  }
+  const int k0 = kb * C::BO;
   const int sq = sk / Hkv, hk = sk - sq * Hkv;
   const SeqSpan sp = seq_span(sh, sq, hk * sh.group);  // the group's first query head
   const int Nq = sp.nq, Nk = sp.nk;
@@ -386,7 +407,7 @@ template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dQ, SeqShape sh,
-    float c, float scale, int nqb, int total) {
+    float c, float scale, int nqb, int total, int chunk) {
   using C = BwdCfg<D>;
   using M = Mfma<BF16>;
   typedef typename M::op8 op8;
@@ -396,9 +417,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
 
   const int logical = xcd_remap(blockIdx.x, total);
-  const int bh = logical / nqb;
-  int qb = logical - bh * nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;  // longest query blocks first
+  int bh, qb;
+  if (CAUSAL) {
+    int rank;
+    heavy_first(logical, nqb, total / nqb, chunk, bh, rank);
+    qb = nqb - 1 - rank;  // the last query block sees the most keys
+  } else {
+    bh = logical / nqb;
+    qb = logical - bh * nqb;
+  }
   const int q0 = qb * C::BO;
   // this (sequence, query head)'s rows; its K/V head is head / group
   const SeqSpan sp = seq_span(sh, bh / sh.H, bh % sh.H);
@@ -545,14 +572,15 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, CAUSAL>), dim3(totk), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
-                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk);
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk,
+                       max(1, totk / nkb / 8));
   const int nqb = (max_nq + C::BO - 1) / C::BO;
   const int totq = nqb * nseq * sh.H;
   if (totq > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL>), dim3(totq), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
-                       static_cast<uint16_t*>(dq), sh, c, scale, nqb, totq);
+                       static_cast<uint16_t*>(dq), sh, c, scale, nqb, totq, max(1, totq / nqb / 8));
   return hipGetLastError();
 }
 
