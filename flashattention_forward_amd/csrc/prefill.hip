@@ -123,11 +123,23 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   // work item: one 256-row query block of one (batch, head).  A paired causal
   // grid puts block nqb-1-j and block j in one workgroup (heavy one first), so
   // every workgroup walks the same number of key tiles; otherwise causal blocks
-  // of a head are taken longest first.
-  const int logical = xcd_remap(blockIdx.x, total);
+  // of a head are taken longest first.  Dense batches give each XCD a
+  // contiguous range of heads (their K/V stay in its L2).  Packed batches, whose
+  // sequences differ in length, instead take block rank j slowest over all
+  // (sequence, head) pairs in plain dispatch order: the longest blocks of every
+  // sequence start first and spread over all XCDs.
+  const bool packed = sh.cu_q != nullptr;
+  const int logical = packed ? (int)blockIdx.x : xcd_remap(blockIdx.x, total);
   const int per_head = paired ? (nqb + 1) / 2 : nqb;
-  const int bh = logical / per_head;
-  const int j_item = logical - bh * per_head;
+  int bh, j_item;
+  if (packed) {
+    const int nh = total / per_head;
+    j_item = logical / nh;
+    bh = logical - j_item * nh;
+  } else {
+    bh = logical / per_head;
+    j_item = logical - bh * per_head;
+  }
   const int nitems = (paired && nqb - 1 - j_item != j_item) ? 2 : 1;
   // this (sequence, head)'s rows; Nq and Nk are its own lengths from here on
   const SeqSpan sp = seq_span(sh, bh / sh.H, bh % sh.H);
