@@ -330,7 +330,17 @@ def main():
         other["varlen_mix_causal"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(fl / per[0] / 1e12, 3),
                                       "frac_peak": round(fl / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4),
                                       "tokens": tot, "sequences": 16, "flops": fl}
-        del tq, tk, tv, o, l, cu
+        # its backward
+        tdo = G.to_torch(G.draw_tensor(wv, "do", threads=16)[0], "bf16")
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(32 * tot * 8, device="cuda", dtype=torch.uint8)
+        _, per = timed_launches([lambda: F.attn_bwd_varlen(tq, tk, tv, o, tdo, l, cu, cu, mx, mx, causal=True,
+                                                           scale=wv.scale, dq=dq, dk=dk, dv=dv, workspace=ws)],
+                                max(5, args.steps // 2), args.warmup)
+        other["backward_varlen_mix_causal"] = {"ms": round(per[0] * 1e3, 4),
+                                               "tflops": round(2.5 * fl / per[0] / 1e12, 3),
+                                               "frac_peak": round(2.5 * fl / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del tq, tk, tv, o, l, cu, tdo, dq, dk, dv, ws
         torch.cuda.empty_cache()
         # grouped-query decode: 32 query heads on 8 K/V heads; GB/s over the K/V bytes
         # that must be read once (the 8 K/V heads)

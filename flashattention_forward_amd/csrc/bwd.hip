@@ -167,10 +167,13 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
 
   // work item: 128 keys of one (sequence, K/V head); the group's query heads
   // all read them, so dK and dV sum over the group's queries
-  const int logical = xcd_remap(blockIdx.x, total);
+  // packed batches: plain dispatch order and one chunk of all heads, so the
+  // longest blocks of every sequence start first on every XCD
+  const bool packed = sh.cu_q != nullptr;
+  const int logical = packed ? (int)blockIdx.x : xcd_remap(blockIdx.x, total);
   const int Hkv = sh.H / sh.group;
   int sk, kb;
-  if (CAUSAL) {
+  if (CAUSAL || packed) {
     heavy_first(logical, nkb, total / nkb, chunk, sk, kb);  // key block 0 has the most queries
   } else {
     sk = logical / nkb;
@@ -416,9 +419,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char v0s[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
 
-  const int logical = xcd_remap(blockIdx.x, total);
+  const bool packed = sh.cu_q != nullptr;
+  const int logical = packed ? (int)blockIdx.x : xcd_remap(blockIdx.x, total);
   int bh, qb;
-  if (CAUSAL) {
+  if (CAUSAL || packed) {
     int rank;
     heavy_first(logical, nqb, total / nqb, chunk, bh, rank);
     qb = nqb - 1 - rank;  // the last query block sees the most keys
@@ -573,14 +577,15 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk,
-                       max(1, totk / nkb / 8));
+                       sh.cu_q != nullptr ? totk / nkb : max(1, totk / nkb / 8));
   const int nqb = (max_nq + C::BO - 1) / C::BO;
   const int totq = nqb * nseq * sh.H;
   if (totq > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL>), dim3(totq), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
-                       static_cast<uint16_t*>(dq), sh, c, scale, nqb, totq, max(1, totq / nqb / 8));
+                       static_cast<uint16_t*>(dq), sh, c, scale, nqb, totq,
+                       sh.cu_q != nullptr ? totq / nqb : max(1, totq / nqb / 8));
   return hipGetLastError();
 }
 
