@@ -35,7 +35,7 @@
 //     tile (S(t) and O += P(t-1) V(t-1), the two streams interleaved), the
 //     other runs the softmax of its previous tile, so the matrix cores and
 //     the vector ALUs of a SIMD (which holds one wave of each group) work at
-//     the same time; a workgroup barrier ends every phase.
+//     the same time; a workgroup barrier ends every tile (every other phase).
 //   * K/V tiles go from global memory straight into LDS (buffer loads with
 //     the LDS-destination form, 1 KB per wave instruction), double-buffered;
 //     only the waves in their MFMA phase issue them, one every other MFMA
@@ -93,8 +93,8 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // phase G_t (S(t) = K(t) Q^T and O += P(t-1) V(t-1): MFMA only) and a softmax
 // phase X_t (mask, running max, exp, row sum of S(t): VALU only).  Group 0
 // runs G_t while group 1 runs X_{t-1}, then group 0 runs X_t while group 1
-// runs G_t, with a workgroup barrier between phases, so on every SIMD one
-// wave feeds the matrix cores while the other feeds the vector ALU.
+// runs G_t, with a workgroup barrier at the end of each tile, so on every SIMD
+// one wave feeds the matrix cores while the other feeds the vector ALU.
 // one 1 KB direct global -> LDS load: lane i's 16 bytes at voff land at dst + 16 i
 // (a free function: the same builtin called from a lambda in the kernel made
 // the host compilation pass drop the kernel's launch stub)
@@ -366,14 +366,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         }
       }
       if (!EVEN) {
-        // the tile loads issued in phase p-1 have landed in every wave's part of LDS
+        // once per tile: the tile loads issued in phase p-1 have landed in every
+        // wave's part of LDS, and every wave is done with the buffers they replace
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-      } else {
-        // phase alignment only: nothing read in phase p+1 was written in phase p,
-        // so no fence (a fence would make this barrier wait for the loads just issued)
-        __builtin_amdgcn_s_barrier();
       }
+      // no barrier after even phases: nothing read in phase p+1 was written in
+      // phase p, and letting the groups drift within a tile measured faster
+      // than holding them in step
     };
     const int nphase = 2 * T + 2;  // even
     for (int p = 0; p < nphase; p += 4) {
