@@ -33,12 +33,25 @@ Readings where the sources are silent:
     lands, inside the quantised tolerance);
   * l sums the unquantised P: only the MFMA operand is cast.
 
+All-INT8 variant (the [INT-FA post]'s INT8 GEMMs in place of the floating
+point ones for both products of the attention): steps 1, 3, 4, 5 as above,
+then
+  2'. V per tensor in int8: s_v = max|V| / 127 (fp32), codes =
+      clamp(rint(V / s_v), -127, 127); a zero tensor gets s_v = 0;
+  6'. P8 = rint(127 P) in [0, 127] (P <= 1, its scale is the constant
+      1/127); O = (P8 . V8) * s_v / (127 l); LSE = m + ln l.
+Reading: P is quantised against the final row max here (the kernel raises
+its running max on every increase, so its P also stays <= 1, and the two
+differ only where the 1/127 rounding lands).
+
 Parity status: the E4M3 table is pinned to the format's closed form and to
 torch's float8_e4m3fn; encoding to exhaustive midpoint/tie sweeps and to
 torch's cast; int8 per-token quantisation to torch.round; the exact integer
 scores to a brute-force Python-int loop; the attention steps 4-6 reuse the
 pinned definition's structure and are pinned by the uniform-score and
-one-hot closed forms under quantisation (tests/test_oracle_quant.py).
+one-hot closed forms under quantisation (tests/test_oracle_pins.py); the
+all-INT8 variant's per-tensor int8 to torch.round and its attention to the
+uniform, two-key and one-hot closed forms (tests/test_oracle_variants.py).
 """
 from __future__ import annotations
 
@@ -102,6 +115,23 @@ def quantize_per_tensor_e4m3(x32):
     return e4m3_encode((x32 / s).astype(np.float32)), s
 
 
+def quantize_per_tensor_int8(x32):
+    """Per-tensor symmetric int8 (the all-INT8 variant's V): x32 fp32 (any
+    shape) -> (q8 int8, scale fp32) with s = max|x| / 127 and
+    q = clamp(rint(x / s), -127, 127) in fp32; a zero tensor gets s = 0."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(127.0))
+    if s == 0:
+        return np.zeros(x32.shape, np.int8), s
+    return np.clip(np.rint((x32 / s).astype(np.float32)), -127, 127).astype(np.int8), s
+
+
+def quantize_prob_int8(p) -> np.ndarray:
+    """P in [0, 1] -> rint(127 P), round half to even (values 0 .. 127)."""
+    return np.rint(127.0 * np.asarray(p, np.float64))
+
+
 def qk_int(q8, k8) -> np.ndarray:
     """Exact integer scores Q8 K8^T for one head (int64)."""
     return np.asarray(q8, np.int64) @ np.asarray(k8, np.int64).T
@@ -150,3 +180,41 @@ def attention_q8(q32, k32, v32, scale: float, causal: bool = False):
     O = np.stack(outs).reshape(lead + outs[0].shape)
     L = np.stack(lses).reshape(lead + lses[0].shape)
     return O, L, qi
+
+
+def attention_i8_head(q8, sq, k8, sk, v8, sv, scale: float, causal: bool = False):
+    """All-INT8 steps 3-5, 6' for one head from quantised inputs (v8 int8
+    per-tensor).  Returns (O, LSE) fp64."""
+    Nq, Nk = q8.shape[0], k8.shape[0]
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
+    s = qk_int(q8, k8).astype(np.float64)
+    s = s * np.asarray(sq, np.float64)[:, None] * np.asarray(sk, np.float64)[None, :] * float(scale)
+    if causal:
+        i = np.arange(Nq)[:, None]
+        j = np.arange(Nk)[None, :]
+        s = np.where(j <= i + (Nk - Nq), s, -np.inf)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    o = quantize_prob_int8(p) @ np.asarray(v8, np.float64)
+    return o * (float(sv) / 127.0) / l[:, None], m + np.log(l)
+
+
+def attention_i8(q32, k32, v32, scale: float, causal: bool = False):
+    """Whole all-INT8 forward on [..., N, d] tensors.  Returns (O, LSE,
+    quantised inputs dict(q8, sq, k8, sk, v8, sv))."""
+    q8, sq = quantize_per_token_int8(q32)
+    k8, sk = quantize_per_token_int8(k32)
+    v8, sv = quantize_per_tensor_int8(v32)
+    lead = np.asarray(q32).shape[:-2]
+    n = int(np.prod(lead)) if lead else 1
+    shp = lambda a: a.reshape((n,) + a.shape[len(lead):])
+    outs, lses = [], []
+    for i in range(n):
+        o, l = attention_i8_head(shp(q8)[i], shp(sq)[i], shp(k8)[i], shp(sk)[i], shp(v8)[i], sv, scale, causal)
+        outs.append(o)
+        lses.append(l)
+    O = np.stack(outs).reshape(lead + outs[0].shape)
+    L = np.stack(lses).reshape(lead + lses[0].shape)
+    return O, L, dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)

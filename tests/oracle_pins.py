@@ -563,3 +563,60 @@ def pin_varlen_backward(bwd_varlen, fwd_varlen, h=1e-5, tol=2e-8):
 
 GQA_PINS = [pin_gqa_repeat, pin_gqa_torch]
 VARLEN_PINS = [pin_varlen_per_sequence, pin_varlen_empty_rows]
+
+
+
+# ---------------------------------------------------------------- all-INT8 variant
+
+def pin_int8_per_tensor(quantize):
+    """Per-tensor int8 against torch's round (half to even) of the fp32
+    quotient (library), the closed form max |x| -> +-127, and a zero tensor."""
+    x = (_RNG.standard_normal((7, 33)) * 3).astype(np.float32)
+    x[2, 5] = -12.5
+    q8, s = quantize(x)
+    assert s == np.float32(np.float32(12.5) / np.float32(127.0)) and q8[2, 5] == -127
+    want = torch.clamp(torch.round(torch.from_numpy(x) / torch.tensor(s)), -127, 127).to(torch.int8).numpy()
+    assert np.array_equal(q8, want)
+    # ties: x / s landing on k + 1/2 exactly goes to the even integer
+    x = np.array([127.0, 2.5, 3.5, -0.5, 0.25], np.float32)
+    q8, s = quantize(x)
+    assert s == np.float32(1.0) and list(q8) == [127, 2, 4, 0, 0]
+    q8, s = quantize(np.zeros((3, 4), np.float32))
+    assert s == 0 and not q8.any()
+
+
+def pin_i8_attention(attn_i8, tol=1e-13):
+    """Closed forms of the all-INT8 steps: (a) Q8 = 0 gives P = 1, P8 = 127
+    for every key, so O = s_v * mean(V8) and LSE = ln Nk; (b) two keys with
+    P = (1, 0.3): P8 = (127, 38), O = s_v (127 v0 + 38 v1) / (127 * 1.3);
+    (c) one key dominant by far: O = s_v * its V8 row."""
+    Nk, d = 9, 8
+    v8 = _RNG.integers(-127, 128, (Nk, d)).astype(np.int8)
+    sv = np.float32(0.25)
+    k8 = _RNG.integers(-127, 128, (Nk, d)).astype(np.int8)
+    O, L = attn_i8(np.zeros((3, d), np.int8), np.full(3, 0.1, np.float32), k8, np.full(Nk, 0.1, np.float32),
+                   v8, sv, 0.5)
+    assert np.max(np.abs(O - 0.25 * v8.astype(np.float64).mean(axis=0))) <= tol
+    assert np.max(np.abs(L - math.log(Nk))) <= tol
+    k8 = np.zeros((2, d), np.int8)
+    k8[:, 0] = 1
+    q8 = np.zeros((1, d), np.int8)
+    q8[0, 0] = 1
+    sk = np.array([1.0, np.float32(1.0 + math.log(0.3))], np.float32)
+    v2 = np.array([[10] * d, [-20] * d], np.int8)
+    O, _ = attn_i8(q8, np.array([1.0], np.float32), k8, sk, v2, np.float32(1.0), 1.0)
+    p1 = math.exp(float(sk[1]) - 1.0)
+    assert round(127 * p1) == 38
+    assert abs(O[0, 0] - (127 * 10 + 38 * -20) / (127.0 * (1.0 + p1))) <= 1e-12
+    # P = 0.7: 127 P = 88.9 rounds to 89 (a floor would give 88)
+    sk = np.array([1.0, np.float32(1.0 + math.log(0.7))], np.float32)
+    O, _ = attn_i8(q8, np.array([1.0], np.float32), k8, sk, v2, np.float32(1.0), 1.0)
+    p1 = math.exp(float(sk[1]) - 1.0)
+    assert round(127 * p1) == 89
+    assert abs(O[0, 0] - (127 * 10 + 89 * -20) / (127.0 * (1.0 + p1))) <= 1e-12
+    k8 = np.zeros((Nk, d), np.int8)
+    k8[np.arange(d), np.arange(d)] = 127
+    q8 = np.zeros((1, d), np.int8)
+    q8[0, 3] = 127
+    O, _ = attn_i8(q8, np.array([0.05], np.float32), k8, np.full(Nk, 0.05, np.float32), v8, sv, 1.0)
+    assert np.max(np.abs(O[0] - 0.25 * v8[3].astype(np.float64))) <= tol

@@ -113,3 +113,54 @@ def test_varlen_mistake_is_caught(mistake):
         except (AssertionError, ValueError):
             failed.append(pin.__name__)
     assert failed
+
+
+# ---- all-INT8 quantised variant
+from oracle import quant as Q
+
+
+def test_int8_per_tensor_pin():
+    P.pin_int8_per_tensor(Q.quantize_per_tensor_int8)
+
+
+def test_i8_attention_pin():
+    P.pin_i8_attention(Q.attention_i8_head)
+
+
+def i8_variant(q8, sq, k8, sk, v8, sv, scale, causal=False, mistake=None):
+    s = Q.qk_int(q8, k8).astype(np.float64) * sq[:, None].astype(np.float64) * sk[None, :].astype(np.float64) * scale
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    p8 = {"floor_p": np.floor(127 * p), "scale_128": np.rint(128 * p)}.get(mistake, np.rint(127 * p))
+    div = 1.0 if mistake == "no_127" else 127.0
+    o = p8 @ v8.astype(np.float64) * (float(sv) / div)
+    return (o if mistake == "no_normalise" else o / l[:, None]), m + np.log(l)
+
+
+def test_unmutated_i8_copy_equals_oracle():
+    rng = np.random.default_rng(11)
+    q8 = rng.integers(-127, 128, (5, 8)).astype(np.int8)
+    k8 = rng.integers(-127, 128, (7, 8)).astype(np.int8)
+    v8 = rng.integers(-127, 128, (7, 8)).astype(np.int8)
+    sq, sk = np.full(5, 0.01, np.float32), np.full(7, 0.02, np.float32)
+    for a, b in zip(i8_variant(q8, sq, k8, sk, v8, np.float32(0.3), 0.5),
+                    Q.attention_i8_head(q8, sq, k8, sk, v8, np.float32(0.3), 0.5)):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("mistake", ["floor_p", "scale_128", "no_127", "no_normalise"])
+def test_i8_mistake_is_caught(mistake):
+    with pytest.raises(AssertionError):
+        P.pin_i8_attention(lambda *a, **kw: i8_variant(*a, **kw, mistake=mistake))
+
+
+def test_int8_per_tensor_mistake_is_caught():
+    def floor_q(x):
+        x = np.asarray(x, np.float32)
+        s = np.float32(np.float32(np.max(np.abs(x))) / np.float32(127.0)) if x.size else np.float32(0)
+        if s == 0:
+            return np.zeros(x.shape, np.int8), s
+        return np.clip(np.floor(x / s), -127, 127).astype(np.int8), s
+    with pytest.raises(AssertionError):
+        P.pin_int8_per_tensor(floor_q)
