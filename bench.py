@@ -18,8 +18,9 @@ Printed as ONE JSON line, which also carries
     prefill configuration (algorithmic FLOPs of its five matrix products,
     2.5x the forward's), grouped-query prefill and decode (32 query heads on
     8 K/V heads), a packed variable-length causal batch, the split-KV decode
-    (GB/s over the K+V bytes) and the quantised forward, each timed the same
-    way (informational).
+    (GB/s over the K+V bytes) and the two quantised forwards (int8 scores
+    with fp8 P.V, and the all-INT8 form), each timed the same way
+    (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
                        [--copy-calibration]
@@ -392,7 +393,13 @@ def main():
         other["quant_8k"] = {"ms": round(per[0] * 1e3, 4), "tops": round(ops / per[0] / 1e12, 3),
                              "frac_fp8_peak": round(ops / per[0] / 1e12 / PEAK_FP8_TFLOPS, 4),
                              "quantize_ms": round(perq[0] * 1e3, 4)}
-        del tq, tk, tv, q8, k8, v8, sq, sk, sv, o, l
+        # the all-INT8 variant on the same inputs (int8 per-tensor V, int8 P)
+        v8i, svi = F.quantize_tensor_i8(tv)
+        _, per = timed_launches([lambda: F.attn_fwd_i8(q8, k8, v8i, sq, sk, svi, scale=wq.scale, out=o, lse=l)],
+                                args.steps, args.warmup)
+        other["quant_i8_8k"] = {"ms": round(per[0] * 1e3, 4), "tops": round(ops / per[0] / 1e12, 3),
+                                "frac_int8_peak": round(ops / per[0] / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        del tq, tk, tv, q8, k8, v8, sq, sk, sv, o, l, v8i, svi
         torch.cuda.empty_cache()
         res["other_workloads"] = other
 

@@ -37,6 +37,8 @@ SIGNATURES = {
     "attn_quantize_e4m3_workspace_bytes": (_Z, [_L]),
     "attn_quantize_tensor_e4m3": (_I, [_P, _P, _P, _L, _P, _Z, _P]),
     "attn_fwd_q8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_fwd_i8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_quantize_tensor_i8": (_I, [_P, _P, _P, _L, _P, _Z, _P]),
     "attn_debug_qk_i32": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_debug_cvt_e4m3": (_I, [_P, _P, _L, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
@@ -297,6 +299,40 @@ def attn_fwd_q8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, sca
                            _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
                            B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
     _check(rc, "attn_fwd_q8")
+    return out, lse
+
+
+def quantize_tensor_i8(x, workspace=None):
+    """Per-tensor int8 of a bf16 tensor -> (int8 codes, fp32 scale as a 1-element GPU tensor)."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16:
+        raise ValueError("quantize_tensor_i8 takes bf16")
+    n = x.numel()
+    x8 = torch.empty(x.shape, device=x.device, dtype=torch.int8)
+    s = torch.empty(1, device=x.device, dtype=torch.float32)
+    wsb = int(lib().attn_quantize_e4m3_workspace_bytes(n))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), device=x.device, dtype=torch.uint8)
+    _check(lib().attn_quantize_tensor_i8(_dev(x, "x"), _dev(x8, "x8"), _dev(s, "scale"), n,
+                                         _dev(workspace, "workspace"), workspace.numel(), _stream()),
+           "attn_quantize_tensor_i8")
+    return x8, s
+
+
+def attn_fwd_i8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
+                out=None, lse=None):
+    """All-INT8 forward: int8 q8/k8 [B,H,N,d] with per-token scales, int8 v8 with a
+    per-tensor scale (1-element GPU tensor).  Returns (O bf16, LSE fp32)."""
+    torch = _torch()
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
+    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
+    rc = lib().attn_fwd_i8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
+                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
+                           B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
+    _check(rc, "attn_fwd_i8")
     return out, lse
 
 

@@ -231,7 +231,29 @@ int attn_fwd_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8, const flo
     return ATTN_E_INVALID;
   if (d != 128) return ATTN_E_UNSUPPORTED;
   return hip_status(attn::launch_prefill_q8(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, B, H, Nq, Nk, d, scale,
-                                            causal != 0, static_cast<hipStream_t>(stream)));
+                                            causal != 0, false, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_i8(const int8_t* q8, const int8_t* k8, const int8_t* v8, const float* q_scale, const float* k_scale,
+                const float* v_scale, void* out, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                int causal, void* stream) {
+  int rc = check_common(q8, k8, v8, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (!q_scale || !k_scale || !v_scale || !aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale))
+    return ATTN_E_INVALID;
+  if (d != 128) return ATTN_E_UNSUPPORTED;
+  return hip_status(attn::launch_prefill_q8(q8, k8, reinterpret_cast<const uint8_t*>(v8), q_scale, k_scale, v_scale,
+                                            out, lse, B, H, Nq, Nk, d, scale, causal != 0, true,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int attn_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!x || !x8 || !scale_out || n < 8 || n % 8 != 0) return ATTN_E_INVALID;
+  if (!aligned16(x) || !aligned16(x8) || !aligned4(scale_out)) return ATTN_E_INVALID;
+  if (!workspace || workspace_bytes < attn::quantize_e4m3_workspace_bytes(n) || !aligned4(workspace))
+    return ATTN_E_WORKSPACE;
+  return hip_status(attn::launch_quantize_tensor_i8(x, x8, scale_out, n, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int attn_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d, void* stream) {

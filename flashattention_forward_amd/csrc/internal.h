@@ -74,10 +74,14 @@ hipError_t launch_quantize_rows_i8(const void* x, int8_t* x8, float* scales, lon
 size_t quantize_e4m3_workspace_bytes(long n);
 hipError_t launch_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_out, long n,
                                        void* workspace, hipStream_t stream);
+// v_int8: V8 holds per-tensor int8 codes and P . V runs in int8 (the all-INT8
+// variant); otherwise V8 holds E4M3 codes and P . V runs in fp8.
 hipError_t launch_prefill_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                              const float* q_scale, const float* k_scale, const float* v_scale,
                              void* out, float* lse, int B, int H, int Nq, int Nk, int d,
-                             float scale, bool causal, hipStream_t stream);
+                             float scale, bool causal, bool v_int8, hipStream_t stream);
+hipError_t launch_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n, void* workspace,
+                                     hipStream_t stream);
 hipError_t launch_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d,
                                hipStream_t stream);
 hipError_t launch_debug_cvt_e4m3(const float* x, uint8_t* y, long n, hipStream_t stream);

@@ -166,6 +166,32 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const uint16_t* __re
   }
 }
 
+// per-tensor symmetric int8 (the all-INT8 variant's V): s = max|x| / 127,
+// codes clamp(rint(x / s), -127, 127), IEEE fp32 division
+__global__ __launch_bounds__(256) void quantize_i8_tensor_kernel(const uint16_t* __restrict__ X, long chunks,
+                                                                 const float* __restrict__ partial, int npart,
+                                                                 int8_t* __restrict__ X8, float* __restrict__ scale_out) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < npart; i += 256) m = fmaxf(m, partial[i]);
+  m = block_max_256(m, red);
+  const float s = m / 127.0f;  // IEEE division
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  for (long c = (long)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (long)gridDim.x * 256) {
+    u32x2 o = {0u, 0u};
+    if (s > 0.f) {
+      float f[8];
+      bf16x8_to_f32(reinterpret_cast<const u32x4*>(X)[c], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float q = fminf(fmaxf(__builtin_rintf(f[j] / s), -127.f), 127.f);
+        o[j >> 2] |= ((uint32_t)((int)q) & 0xFFu) << (8 * (j & 3));
+      }
+    }
+    reinterpret_cast<u32x2*>(X8)[c] = o;
+  }
+}
+
 __global__ __launch_bounds__(256) void debug_cvt_e4m3_kernel(const float* __restrict__ x, uint8_t* __restrict__ y, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (2 * i + 1 < n) {
@@ -248,7 +274,22 @@ struct Q8Stage {
   }
 };
 
-template <bool CAUSAL>
+// rint(127 p) of four probabilities p in [0, 1] as bytes (P's scale is the
+// constant 1/127 in the all-INT8 variant)
+__device__ __forceinline__ uint32_t p_u8x4(float a, float b, float c, float d) {
+  const uint32_t x0 = (uint32_t)__builtin_rintf(127.f * a), x1 = (uint32_t)__builtin_rintf(127.f * b);
+  const uint32_t x2 = (uint32_t)__builtin_rintf(127.f * c), x3 = (uint32_t)__builtin_rintf(127.f * d);
+  return x0 | (x1 << 8) | (x2 << 16) | (x3 << 24);
+}
+
+// I8V: the all-INT8 variant -- V8 holds per-tensor int8 codes and P . V runs
+// on the int8 MFMA: P is quantised as rint(127 P), which needs P <= 1, so the
+// running max is raised on every increase (no lazy threshold); each 64-key
+// tile is two 32-key int8 steps whose operands are the two halves of the
+// E4M3 form's (same key order), and the exact int32 tile product is added
+// into the fp32 accumulator (a float rescale of an int32 running sum would
+// not be exact).
+template <bool CAUSAL, bool I8V>
 __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
     const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
@@ -327,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
       mt = pair_max(mt) * cq;
-      if (__any(mt > m_run + kRescaleThresholdQ)) {
+      if (__any(mt > m_run + (I8V ? 0.f : kRescaleThresholdQ))) {
         const float mn = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
@@ -346,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
         const float p2 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 2], cq, -m_use));
         const float p3 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 3], cq, -m_use));
         l_run += (p0 + p1) + (p2 + p3);
-        pb[jw] = (int)e4m3x4(p0, p1, p2, p3);
+        pb[jw] = I8V ? (int)p_u8x4(p0, p1, p2, p3) : (int)e4m3x4(p0, p1, p2, p3);
       }
       // O^T += V^T P^T: lane (h, d) reads LDS rows 32h .. 32h+31 at column d
       const int r16 = lane & 15, g1 = (lane >> 4) & 1;
@@ -360,7 +401,16 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
           a[2 * r] = x[0];
           a[2 * r + 1] = x[1];
         }
-        o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 0, 0, 127, 0, 127);
+        if (I8V) {
+          i32x16 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[0], a[1], a[2], a[3]},
+                                                             i32x4{pb[0], pb[1], pb[2], pb[3]}, i32x16{}, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[4], a[5], a[6], a[7]}, i32x4{pb[4], pb[5], pb[6], pb[7]},
+                                                      acc, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[mb][j] += (float)acc[j];  // |acc| < 64 * 127^2 < 2^24: exact
+        } else {
+          o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 0, 0, 127, 0, 127);
+        }
       }
     }
     __syncthreads();
@@ -371,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
   }
 
   const float l_tot = pair_sum(l_run);
-  const float f = *VS / l_tot;
+  const float f = I8V ? *VS / (127.f * l_tot) : *VS / l_tot;
   if (qrow < Nq) {
     uint16_t* dst = O + (qbase + qrow) * C::D;
 #pragma unroll
@@ -452,16 +502,34 @@ hipError_t launch_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_
 
 hipError_t launch_prefill_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8, const float* q_scale,
                              const float* k_scale, const float* v_scale, void* out, float* lse, int B, int H, int Nq,
-                             int Nk, int d, float scale, bool causal, hipStream_t stream) {
+                             int Nk, int d, float scale, bool causal, bool v_int8, hipStream_t stream) {
   if (d != Q8Cfg::D) return hipErrorInvalidValue;
   const int nqb = (Nq + Q8Cfg::BM - 1) / Q8Cfg::BM;
   const int total = nqb * B * H;
-  if (causal)
-    hipLaunchKernelGGL(prefill_q8_kernel<true>, dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8, q_scale, k_scale,
-                       v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb, total);
-  else
-    hipLaunchKernelGGL(prefill_q8_kernel<false>, dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8, q_scale, k_scale,
-                       v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb, total);
+#define ATTN_Q8(CA_, I8_)                                                                                      \
+  if (causal == CA_ && v_int8 == I8_)                                                                          \
+    hipLaunchKernelGGL((prefill_q8_kernel<CA_, I8_>), dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8,     \
+                       q_scale, k_scale, v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb, \
+                       total);
+  ATTN_Q8(true, false)
+  ATTN_Q8(false, false)
+  ATTN_Q8(true, true)
+  ATTN_Q8(false, true)
+#undef ATTN_Q8
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n, void* workspace,
+                                     hipStream_t stream) {
+  const long chunks = n / 8;
+  const int g = e4m3_grid(n);
+  float* partial = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(256), 0, stream, static_cast<const uint16_t*>(x), chunks,
+                     partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quantize_i8_tensor_kernel, dim3(g), dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+                     chunks, partial, g, x8, scale_out);
   return hipGetLastError();
 }
 

@@ -245,6 +245,33 @@ int attn_fwd_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                 float scale, int causal, void* stream);
 
 /*
+ * All-INT8 quantised forward: both products of the attention as INT8 GEMMs,
+ * the INT-FlashAttention scheme of the hoodcat.net post "INT-FlashAttention:
+ * an INT8 quantisation architecture compatible with FlashAttention".  Scores
+ * as in attn_fwd_q8; V in int8 with one per-tensor scale
+ * (attn_quantize_tensor_i8); P = exp(S - running max), kept <= 1 by raising
+ * the running max on every increase, is quantised as rint(127 P) and P.V is
+ * accumulated exactly in int32 per 64-key tile on int8 MFMA;
+ * O = (sum of tiles) * v_scale / (127 l) with l the sum of the fp32 P.
+ *   q8, k8 as attn_fwd_q8; v8 [B,H,Nk,d] int8; v_scale DEVICE pointer to
+ *   one float32; out, lse, d, causal and errors as attn_fwd_q8.
+ */
+int attn_fwd_i8(const int8_t* q8, const int8_t* k8, const int8_t* v8,
+                const float* q_scale, const float* k_scale, const float* v_scale,
+                void* out, float* lse, int B, int H, int Nq, int Nk, int d,
+                float scale, int causal, void* stream);
+
+/*
+ * Per-tensor int8 for attn_fwd_i8's V: x [n] bf16 -> x8 [n] int8 and
+ * *scale_out (DEVICE float) with s = max|x| / 127 and
+ * x8 = clamp(rint(x / s), -127, 127) (IEEE fp32 division, round half to
+ * even); an all-zero tensor gives s = 0 and x8 = 0.  n >= 8, a multiple of
+ * 8; workspace as attn_quantize_tensor_e4m3 (the partial maxima).
+ */
+int attn_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hooks that expose the quantised kernel's own device code:
  * attn_debug_qk_i32: s[i,j] = sum_t q8[i,t] k8[j,t] for one head
  *   (q8 [Nq,d], k8 [Nk,d] int8, s [Nq,Nk] int32), through the same int8

@@ -106,6 +106,21 @@ def test_quant_entry_points_reject():
     assert L.attn_quantize_tensor_e4m3(A, A, A, 12, A, 4096, None) == Bd.ATTN_E_INVALID
     assert L.attn_quantize_tensor_e4m3(A, A, A, 1 << 20, A, 4, None) == Bd.ATTN_E_WORKSPACE
     assert L.attn_quantize_tensor_e4m3(A, A, A, 1 << 20, None, 1 << 20, None) == Bd.ATTN_E_WORKSPACE
+    i8 = lambda **kw: L.attn_fwd_i8(kw.get("q", A), A, kw.get("v", A), A, kw.get("ks", A), kw.get("vs", A), A, A,
+                                    1, 1, kw.get("Nq", 8), 8, kw.get("d", 128), kw.get("scale", 0.1),
+                                    kw.get("causal", 0), None)
+    assert i8(d=64) == Bd.ATTN_E_UNSUPPORTED
+    assert i8(ks=None) == Bd.ATTN_E_INVALID
+    assert i8(vs=None) == Bd.ATTN_E_INVALID
+    assert i8(vs=A + 2) == Bd.ATTN_E_INVALID  # scale pointers need 4-byte alignment
+    assert i8(v=None) == Bd.ATTN_E_INVALID
+    assert i8(Nq=9, causal=1) == Bd.ATTN_E_INVALID
+    assert i8(scale=float("inf")) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_tensor_i8(A, A, A, 12, A, 4096, None) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_tensor_i8(A, A, A, 0, A, 4096, None) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_tensor_i8(MIS, A, A, 1 << 20, A, 1 << 20, None) == Bd.ATTN_E_INVALID
+    assert L.attn_quantize_tensor_i8(A, A, A, 1 << 20, A, 4, None) == Bd.ATTN_E_WORKSPACE
+    assert L.attn_quantize_tensor_i8(A, A, A, 1 << 20, None, 1 << 20, None) == Bd.ATTN_E_WORKSPACE
     assert L.attn_debug_qk_i32(A, A, A, 4, 4, 64, None) == Bd.ATTN_E_UNSUPPORTED
     assert L.attn_debug_qk_i32(None, A, A, 4, 4, 128, None) == Bd.ATTN_E_INVALID
     assert L.attn_debug_cvt_e4m3(A, A, 3, None) == Bd.ATTN_E_INVALID

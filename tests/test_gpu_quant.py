@@ -148,3 +148,123 @@ def test_q8_full_size_sampled(F):
         assert np.abs(l_all[b, h, rows] - L).max() <= LSE_TOL
     print(f"  sampled max|dO|={worst:.3e}", flush=True)
     assert worst <= QO_TOL
+
+
+# ---- all-INT8 variant: int8 V per tensor, P quantised as rint(127 P) ------
+
+def _quantize_i8_on_gpu(F, q, k, v):
+    import torch
+    from tests.gpu_util import to_dev
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    q8, sq = F.quantize_rows_i8(tq)
+    k8, sk = F.quantize_rows_i8(tk)
+    v8, sv = F.quantize_tensor_i8(tv)
+    torch.cuda.synchronize()
+    return q8, sq, k8, sk, v8, sv
+
+
+def test_i8_tensor_quantisation_bit_exact(F):
+    """Per-tensor int8 codes and scale equal the oracle's, including the
+    extreme codes +-127, values near the rounding midpoints and an all-zero
+    tensor (scale 0, codes 0)."""
+    import torch
+    from tests.gpu_util import to_dev
+    rng = np.random.default_rng(64)
+    x = (rng.standard_normal(4096 * 8) * 3).astype(np.float32)
+    x[0], x[1] = 5.0, -5.0              # s = 5/127: +-127 exactly
+    x[2:10] = (np.arange(8) + 0.5) * np.float32(5.0 / 127.0)  # near the midpoints (after bf16 rounding)
+    for arr in (x, np.zeros(64, np.float32)):
+        bits = G.round_to_bf16_bits(arr)
+        t = to_dev(bits, "bf16")
+        ref8, refs = Q.quantize_per_tensor_int8(G.to_f32(bits, "bf16"))
+        print(f"  gpu: quantize_tensor_i8 n={arr.size}", flush=True)
+        x8, s = F.quantize_tensor_i8(t)
+        torch.cuda.synchronize()
+        assert s.cpu().numpy()[0] == refs
+        assert np.array_equal(x8.cpu().numpy(), ref8)
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 2, 300, 300), False), ((2, 1, 77, 333), True),
+                                          ((1, 1, 128, 64), False), ((1, 2, 200, 1000), False),
+                                          ((1, 1, 260, 260), True), ((1, 1, 1, 1), False)],
+                         ids=lambda x: str(x))
+def test_i8_small(F, shape, causal):
+    import torch
+    from tests.gpu_util import errors, from_dev
+    B, H, Nq, Nk = shape
+    w = G.Workload("i8_small", 65, B, H, Nq, Nk, 128, "bf16", 1.0, causal, 128 ** -0.5)
+    q, k, v = G.draw_qkv(w)
+    f32 = lambda x: G.to_f32(x, "bf16")
+    O, L, qi = Q.attention_i8(f32(q), f32(k), f32(v), w.scale, causal)
+    q8, sq, k8, sk, v8, sv = _quantize_i8_on_gpu(F, q, k, v)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    print(f"  gpu: attn_fwd_i8 {shape} causal={causal}", flush=True)
+    out, lse = F.attn_fwd_i8(q8, k8, v8, sq, sk, sv, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    eo, ro = errors(from_dev(out), O)
+    el, _ = errors(from_dev(lse), L)
+    print(f"  max|dO|={eo:.3e} (rel {ro:.3e}) max|dLSE|={el:.3e}", flush=True)
+    assert eo <= QO_TOL and el <= LSE_TOL
+
+
+def test_i8_peaked_rows(F):
+    """Rows whose scores are dominated by one key (P near one-hot: P8 = 127
+    for it, small integers elsewhere) and rows of equal scores (uniform P):
+    the two ends of the 1/127 grid."""
+    import torch
+    from tests.gpu_util import from_dev
+    w = G.Workload("i8_peak", 66, 1, 1, 192, 256, 128, "bf16", 1.0, False, 128 ** -0.5)
+    q, k, v = G.draw_qkv(w)
+    q[0, 0, :64] = G.round_to_bf16_bits(G.to_f32(q[0, 0, :64], "bf16") * 8)  # sharp rows
+    q[0, 0, 64:128] = 0                    # zero rows: scale 0, uniform P
+    f32 = lambda x: G.to_f32(x, "bf16")
+    O, L, qi = Q.attention_i8(f32(q), f32(k), f32(v), w.scale)
+    q8, sq, k8, sk, v8, sv = _quantize_i8_on_gpu(F, q, k, v)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    out, lse = F.attn_fwd_i8(q8, k8, v8, sq, sk, sv, scale=w.scale)
+    torch.cuda.synchronize()
+    eo = np.abs(from_dev(out) - O).max()
+    print(f"  peaked max|dO|={eo:.3e}", flush=True)
+    assert eo <= QO_TOL and np.abs(from_dev(lse) - L).max() <= LSE_TOL
+
+
+def test_i8_full_size_sampled(F):
+    """B=2 H=32 N=8192 d=128 through the all-INT8 path: quantisation
+    bit-exact, sampled rows of sampled heads against the oracle."""
+    import torch
+    from tests.gpu_util import from_dev
+    w = G.WORKLOADS["quant_8k"]
+    q, k, v = G.draw_qkv(w, threads=16)
+    f32 = lambda x: G.to_f32(x, "bf16")
+    q8r, sqr = Q.quantize_per_token_int8(f32(q))
+    k8r, skr = Q.quantize_per_token_int8(f32(k))
+    v8r, svr = Q.quantize_per_tensor_int8(f32(v))
+    qi = dict(q8=q8r, sq=sqr, k8=k8r, sk=skr, v8=v8r, sv=svr)
+    q8, sq, k8, sk, v8, sv = _quantize_i8_on_gpu(F, q, k, v)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    for causal in (False, True):
+        print(f"  gpu: attn_fwd_i8 full size causal={causal}", flush=True)
+        out, lse = F.attn_fwd_i8(q8, k8, v8, sq, sk, sv, causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        o_all, l_all = from_dev(out), from_dev(lse)
+        assert np.isfinite(o_all).all() and np.isfinite(l_all).all()
+        rng = np.random.default_rng(4)
+        worst = 0.0
+        for bh in rng.choice(w.B * w.H, 4, replace=False):
+            b, h = divmod(int(bh), w.H)
+            rows = np.unique(np.concatenate([[0, 8191], rng.integers(0, w.Nq, 32)]))
+            if causal:
+                # the causal oracle takes a prefix of keys per row: one row at a time
+                for r in rows:
+                    O, L = Q.attention_i8_head(qi["q8"][b, h][r:r + 1], qi["sq"][b, h][r:r + 1],
+                                               qi["k8"][b, h][:r + 1], qi["sk"][b, h][:r + 1],
+                                               qi["v8"][b, h][:r + 1], qi["sv"], w.scale)
+                    worst = max(worst, np.abs(o_all[b, h, r] - O[0]).max())
+                    assert abs(l_all[b, h, r] - L[0]) <= LSE_TOL
+            else:
+                O, L = Q.attention_i8_head(qi["q8"][b, h][rows], qi["sq"][b, h][rows], qi["k8"][b, h],
+                                           qi["sk"][b, h], qi["v8"][b, h], qi["sv"], w.scale)
+                worst = max(worst, np.abs(o_all[b, h, rows] - O).max())
+                assert np.abs(l_all[b, h, rows] - L).max() <= LSE_TOL
+        print(f"  sampled max|dO|={worst:.3e}", flush=True)
+        assert worst <= QO_TOL
