@@ -34,7 +34,10 @@ Modules:
                  through the plain definition.
   variants    -- grouped-query heads (GQA/MQA) and packed variable-length
                  batches, by head mapping and slicing of the definition.
+  rotated     -- FP8 attention with Q and K rotated by a random-sign Hadamard
+                 matrix before block quantisation ([trading post], "FA3:
+                 Hopper mechanisms", FP8 with incoherent processing).
 
 Parity status of every function is stated in its module header.
 """
-from . import attention, backward, quant, recurrence, variants  # noqa: F401
+from . import attention, backward, quant, recurrence, rotated, variants  # noqa: F401
