@@ -18,9 +18,9 @@ Printed as ONE JSON line, which also carries
     prefill configuration (algorithmic FLOPs of its five matrix products,
     2.5x the forward's), grouped-query prefill and decode (32 query heads on
     8 K/V heads), a packed variable-length causal batch, the split-KV decode
-    (GB/s over the K+V bytes) and the two quantised forwards (int8 scores
-    with fp8 P.V, and the all-INT8 form), each timed the same way
-    (informational).
+    (GB/s over the K+V bytes) and the three quantised forwards (int8 scores
+    with fp8 P.V, the all-INT8 form, and FP8 with rotated Q and K), each
+    timed the same way (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
                        [--copy-calibration]
@@ -399,7 +399,18 @@ def main():
                                 args.steps, args.warmup)
         other["quant_i8_8k"] = {"ms": round(per[0] * 1e3, 4), "tops": round(ops / per[0] / 1e12, 3),
                                 "frac_int8_peak": round(ops / per[0] / 1e12 / PEAK_FP8_TFLOPS, 4)}
-        del tq, tk, tv, q8, k8, v8, sq, sk, sv, o, l, v8i, svi
+        # rotated FP8 (random-sign Hadamard + block E4M3 of Q and K; V and P as above)
+        sgn = torch.from_numpy(G.draw_signs(90, wq.d)).cuda()
+        f8q, fsq = F.rotate_quantize_e4m3(tq, sgn, 64)
+        f8k, fsk = F.rotate_quantize_e4m3(tk, sgn, 64)
+        _, per = timed_launches([lambda: F.attn_fwd_fp8(f8q, f8k, v8, fsq, fsk, sv, scale=wq.scale, out=o, lse=l)],
+                                args.steps, args.warmup)
+        _, perr = timed_launches([lambda: (F.rotate_quantize_e4m3(tq, sgn, 64), F.rotate_quantize_e4m3(tk, sgn, 64))],
+                                 5, 1)
+        other["quant_fp8_rotated_8k"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(ops / per[0] / 1e12, 3),
+                                         "frac_fp8_peak": round(ops / per[0] / 1e12 / PEAK_FP8_TFLOPS, 4),
+                                         "rotate_quantize_qk_ms": round(perr[0] * 1e3, 4), "block_rows": 64}
+        del tq, tk, tv, q8, k8, v8, sq, sk, sv, o, l, v8i, svi, f8q, f8k, fsq, fsk, sgn
         torch.cuda.empty_cache()
         res["other_workloads"] = other
 

@@ -161,3 +161,28 @@ def to_torch(x: np.ndarray, dtype: str, device: str = "cuda"):
     if dtype == "fp16":
         return torch.from_numpy(np.ascontiguousarray(x)).to(device)
     raise ValueError(dtype)
+
+
+def draw_signs(seed: int, d: int) -> np.ndarray:
+    """d random signs (+1.0 / -1.0, float32): the diagonal of the random
+    rotation applied to Q and K before FP8 block quantisation."""
+    rng = np.random.default_rng([seed, 0x5167])
+    return np.where(rng.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+def outlier_qkv(seed: int, N: int, d: int, kind: str):
+    """One head of Q, K, V [N, d] as bf16 bits, N(0, 1) entries with
+    outliers: 'sparse' sets 0.1 % of the entries of each tensor to N(0, 10)
+    draws; 'channel' multiplies four fixed channels of Q and K by 10 (the
+    same channels for every token); 'none' adds nothing."""
+    if kind not in ("sparse", "channel", "none"):
+        raise ValueError(kind)
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    if kind == "sparse":
+        q, k, v = (np.where(rng.random(x.shape) < 1e-3, rng.standard_normal(x.shape) * 10, x) for x in (q, k, v))
+    elif kind == "channel":
+        ch = rng.choice(d, 4, replace=False)
+        q[:, ch] *= 10
+        k[:, ch] *= 10
+    return tuple(round_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))

@@ -39,7 +39,10 @@ SIGNATURES = {
     "attn_fwd_q8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_fwd_i8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_quantize_tensor_i8": (_I, [_P, _P, _P, _L, _P, _Z, _P]),
+    "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_rotate_quantize_e4m3": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "attn_debug_qk_i32": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "attn_debug_qk_f8": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_debug_cvt_e4m3": (_I, [_P, _P, _L, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_build_info": (ctypes.c_char_p, []),
@@ -336,6 +339,45 @@ def attn_fwd_i8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, sca
     return out, lse
 
 
+def rotate_quantize_e4m3(x, signs=None, block_rows: int = 64):
+    """Block E4M3 codes of a bf16 [..., N, d] tensor, rotated by diag(signs) H_d
+    first when signs (a d-element float32 GPU tensor of +-1) is given ->
+    (uint8 codes [..., N, d], fp32 per-row scales [..., N])."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16:
+        raise ValueError("rotate_quantize_e4m3 takes bf16")
+    *lead, N, d = x.shape
+    BH = int(math.prod(lead)) if lead else 1
+    x8 = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
+    sc = torch.empty((*lead, N), device=x.device, dtype=torch.float32)
+    sp = None
+    if signs is not None:
+        if signs.dtype != torch.float32 or signs.numel() != d:
+            raise ValueError("signs must be d float32 values")
+        sp = _dev(signs, "signs")
+    _check(lib().attn_rotate_quantize_e4m3(_dev(x, "x"), sp, _dev(x8, "x8"), _dev(sc, "scales"), BH, N, d,
+                                           int(block_rows), _stream()), "attn_rotate_quantize_e4m3")
+    return x8, sc
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
+                 out=None, lse=None):
+    """FP8 forward: E4M3 q8/k8 [B,H,N,d] with per-row scales (from
+    rotate_quantize_e4m3), E4M3 v8 with a per-tensor scale (1-element GPU
+    tensor).  Returns (O bf16, LSE fp32)."""
+    torch = _torch()
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
+    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
+    rc = lib().attn_fwd_fp8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
+                            _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
+                            B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
+    _check(rc, "attn_fwd_fp8")
+    return out, lse
+
+
 def debug_qk_i32(q8, k8):
     """int32 Q8 K8^T of one head through the quantised kernel's tile routine."""
     torch = _torch()
@@ -344,6 +386,17 @@ def debug_qk_i32(q8, k8):
     s = torch.empty((Nq, Nk), device=q8.device, dtype=torch.int32)
     _check(lib().attn_debug_qk_i32(_dev(q8, "q8"), _dev(k8, "k8"), _dev(s, "s"), Nq, Nk, d, _stream()),
            "attn_debug_qk_i32")
+    return s
+
+
+def debug_qk_f8(q8, k8):
+    """fp32 scores of one head's E4M3 codes through the fp8 kernel's tile routine."""
+    torch = _torch()
+    Nq, d = q8.shape
+    Nk = k8.shape[0]
+    s = torch.empty((Nq, Nk), device=q8.device, dtype=torch.float32)
+    _check(lib().attn_debug_qk_f8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(s, "s"), Nq, Nk, d, _stream()),
+           "attn_debug_qk_f8")
     return s
 
 

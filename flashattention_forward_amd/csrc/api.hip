@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is launched; an error return
 // means no work was enqueued.  See include/attn_mi355x.h for the contract.
 #include <cmath>
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 
@@ -231,7 +232,8 @@ int attn_fwd_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8, const flo
     return ATTN_E_INVALID;
   if (d != 128) return ATTN_E_UNSUPPORTED;
   return hip_status(attn::launch_prefill_q8(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, B, H, Nq, Nk, d, scale,
-                                            causal != 0, false, static_cast<hipStream_t>(stream)));
+                                            causal != 0, attn::QVariant::kInt8Scores,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd_i8(const int8_t* q8, const int8_t* k8, const int8_t* v8, const float* q_scale, const float* k_scale,
@@ -243,8 +245,31 @@ int attn_fwd_i8(const int8_t* q8, const int8_t* k8, const int8_t* v8, const floa
     return ATTN_E_INVALID;
   if (d != 128) return ATTN_E_UNSUPPORTED;
   return hip_status(attn::launch_prefill_q8(q8, k8, reinterpret_cast<const uint8_t*>(v8), q_scale, k_scale, v_scale,
-                                            out, lse, B, H, Nq, Nk, d, scale, causal != 0, true,
+                                            out, lse, B, H, Nq, Nk, d, scale, causal != 0, attn::QVariant::kAllInt8,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale, const float* k_scale,
+                 const float* v_scale, void* out, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                 int causal, void* stream) {
+  int rc = check_common(q8, k8, v8, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (!q_scale || !k_scale || !v_scale || !aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale))
+    return ATTN_E_INVALID;
+  if (d != 128) return ATTN_E_UNSUPPORTED;
+  return hip_status(attn::launch_prefill_q8(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, B, H, Nq, Nk, d, scale,
+                                            causal != 0, attn::QVariant::kFp8, static_cast<hipStream_t>(stream)));
+}
+
+int attn_rotate_quantize_e4m3(const void* x, const float* signs, uint8_t* x8, float* scales, int BH, int N, int d,
+                              int block_rows, void* stream) {
+  if (!x || !x8 || !scales || BH < 1 || N < 1 || block_rows < 1) return ATTN_E_INVALID;
+  if (!aligned16(x) || !aligned16(x8) || !aligned4(scales) || (signs && !aligned4(signs))) return ATTN_E_INVALID;
+  if (d != 128) return ATTN_E_UNSUPPORTED;
+  const long nblk = (N + (long)std::min(block_rows, N) - 1) / std::min(block_rows, N);
+  if ((long)BH * nblk > 0x7fffffffL) return ATTN_E_INVALID;
+  return hip_status(attn::launch_rotate_quantize_e4m3(x, signs, x8, scales, BH, N, d, block_rows,
+                                                      static_cast<hipStream_t>(stream)));
 }
 
 int attn_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n, void* workspace,
@@ -260,7 +285,14 @@ int attn_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, in
   if (!q8 || !k8 || !s || Nq < 1 || Nk < 1) return ATTN_E_INVALID;
   if (!aligned16(q8) || !aligned16(k8) || !aligned4(s)) return ATTN_E_INVALID;
   if (d != 128) return ATTN_E_UNSUPPORTED;
-  return hip_status(attn::launch_debug_qk_i32(q8, k8, s, Nq, Nk, d, static_cast<hipStream_t>(stream)));
+  return hip_status(attn::launch_debug_qk(q8, k8, s, Nq, Nk, d, false, static_cast<hipStream_t>(stream)));
+}
+
+int attn_debug_qk_f8(const uint8_t* q8, const uint8_t* k8, float* s, int Nq, int Nk, int d, void* stream) {
+  if (!q8 || !k8 || !s || Nq < 1 || Nk < 1) return ATTN_E_INVALID;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned4(s)) return ATTN_E_INVALID;
+  if (d != 128) return ATTN_E_UNSUPPORTED;
+  return hip_status(attn::launch_debug_qk(q8, k8, s, Nq, Nk, d, true, static_cast<hipStream_t>(stream)));
 }
 
 int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream) {

@@ -74,16 +74,24 @@ hipError_t launch_quantize_rows_i8(const void* x, int8_t* x8, float* scales, lon
 size_t quantize_e4m3_workspace_bytes(long n);
 hipError_t launch_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_out, long n,
                                        void* workspace, hipStream_t stream);
-// v_int8: V8 holds per-tensor int8 codes and P . V runs in int8 (the all-INT8
-// variant); otherwise V8 holds E4M3 codes and P . V runs in fp8.
-hipError_t launch_prefill_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
+// The quantised forwards share one kernel: kInt8Scores has int8 Q8/K8 and
+// E4M3 V8 and P (int8 scores, fp8 P . V); kAllInt8 has int8 V8 and P
+// (both products on the int8 MFMA); kFp8 has E4M3 Q8/K8, V8 and P (both
+// products on the fp8 MFMA).
+enum class QVariant : int { kInt8Scores = 0, kAllInt8 = 1, kFp8 = 2 };
+hipError_t launch_prefill_q8(const void* q8, const void* k8, const void* v8,
                              const float* q_scale, const float* k_scale, const float* v_scale,
                              void* out, float* lse, int B, int H, int Nq, int Nk, int d,
-                             float scale, bool causal, bool v_int8, hipStream_t stream);
+                             float scale, bool causal, QVariant variant, hipStream_t stream);
+// Block E4M3 quantisation of x [BH, N, d] bf16, optionally after the
+// random-sign Hadamard rotation (signs != nullptr): per-row scales [BH, N].
+hipError_t launch_rotate_quantize_e4m3(const void* x, const float* signs, uint8_t* x8, float* scales, int BH,
+                                       int N, int d, int block_rows, hipStream_t stream);
 hipError_t launch_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n, void* workspace,
                                      hipStream_t stream);
-hipError_t launch_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d,
-                               hipStream_t stream);
+// s: int32 scores of int8 codes, or fp32 scores of E4M3 codes (fp8)
+hipError_t launch_debug_qk(const void* q8, const void* k8, void* s, int Nq, int Nk, int d, bool fp8,
+                           hipStream_t stream);
 hipError_t launch_debug_cvt_e4m3(const float* x, uint8_t* y, long n, hipStream_t stream);
 
 }  // namespace attn

@@ -21,6 +21,8 @@
 // The quantisation kernels (per-token int8, per-tensor E4M3) and two test
 // hooks that run this file's own tile routines live here as well.
 #include <cfloat>
+#include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -28,8 +30,6 @@
 namespace attn {
 
 namespace {
-
-constexpr float kRescaleThresholdQ = 8.0f;
 
 template <int CTRL>
 __device__ __forceinline__ float dppq(float x) {
@@ -201,6 +201,96 @@ __global__ __launch_bounds__(256) void debug_cvt_e4m3_kernel(const float* __rest
   }
 }
 
+// ------------------------------------------------ rotated block quantisation
+// One row (d = 128) of the unnormalised Walsh-Hadamard transform of x * sigma
+// in fp32, held by 16 lanes: lane j of the group holds elements 8j .. 8j+7.
+// Butterflies (lo, hi) -> (lo + hi, lo - hi) at element strides 1, 2, 4
+// (inside the lane), then 8, 16, 32, 64 (lane strides 1, 2, 4, 8: DPP quad
+// permutes, a 32-lane swizzle and a 16-lane rotation by 8), in that order.
+// Without rotation the row is returned as read.
+template <int CTRL>
+__device__ __forceinline__ void butterfly_x(float* y, bool hi) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float p;
+    if constexpr (CTRL < 0)
+      p = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, y[e]), -CTRL));
+    else
+      p = dppq<CTRL>(y[e]);
+    const float lo = y[e] + p, hv = p - y[e];
+    y[e] = hi ? hv : lo;
+  }
+}
+
+__device__ __forceinline__ void fwht_row128_x16(u32x4 u, const float* sg, bool rot, int j, float* y) {
+  bf16x8_to_f32(u, y);
+  if (!rot) return;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] *= sg[e];  // exact: the signs are +-1
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!(e & h)) {
+        const float lo = y[e], hi = y[e + h];
+        y[e] = lo + hi;
+        y[e + h] = lo - hi;
+      }
+  butterfly_x<0xB1>(y, (j & 1) != 0);      // lane xor 1 (quad_perm 1,0,3,2)
+  butterfly_x<0x4E>(y, (j & 2) != 0);      // lane xor 2 (quad_perm 2,3,0,1)
+  butterfly_x<-0x101F>(y, (j & 4) != 0);   // lane xor 4 (swizzle, bit mode)
+  butterfly_x<0x128>(y, (j & 8) != 0);     // lane xor 8 (row rotate by 8)
+}
+
+// Workgroup = one block of up to R consecutive rows of one head, four rows
+// per wave at a time; pass 1 finds the block's max |y|, pass 2 recomputes the
+// (deterministic) transform and writes E4M3(y / s), s = max / 448 (IEEE fp32
+// division); every row of the block stores s * post (post = 1 / sqrt(d) when
+// rotating, else 1).
+__global__ __launch_bounds__(256) void rotate_quantize_e4m3_kernel(const uint16_t* __restrict__ X,
+                                                                   const float* __restrict__ signs,
+                                                                   uint8_t* __restrict__ X8, float* __restrict__ S,
+                                                                   int N, int R, int nblk, float post) {
+  __shared__ float red[4];
+  const int bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
+  const int r0 = blk * R, r1 = min(N, r0 + R);
+  const int tid = threadIdx.x, j = tid & 15, rg = tid >> 4;  // 16 row slots per pass
+  const bool rot = signs != nullptr;
+  float sg[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sg[e] = rot ? signs[8 * j + e] : 1.f;
+  const uint16_t* Xh = X + (size_t)bh * N * 128;
+  float amax = 0.f;
+  // every lane runs the same trip count (the cross-lane steps need the whole
+  // row group); rows past the block read as zero and are not stored
+  const int npass = (r1 - r0 + 15) / 16;
+  for (int it = 0; it < npass; ++it) {
+    const int r = r0 + 16 * it + rg;
+    const u32x4 u = r < r1 ? reinterpret_cast<const u32x4*>(Xh + (size_t)r * 128)[j] : u32x4{0u, 0u, 0u, 0u};
+    float y[8];
+    fwht_row128_x16(u, sg, rot, j, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+  }
+  amax = block_max_256(amax, red);
+  const float sc = amax / 448.0f;
+  const float stored = rot ? sc * post : sc;
+  for (int r = r0 + tid; r < r1; r += 256) S[(size_t)bh * N + r] = stored;
+  uint8_t* X8h = X8 + (size_t)bh * N * 128;
+  for (int it = 0; it < npass; ++it) {
+    const int r = r0 + 16 * it + rg;
+    const u32x4 u = r < r1 ? reinterpret_cast<const u32x4*>(Xh + (size_t)r * 128)[j] : u32x4{0u, 0u, 0u, 0u};
+    float y[8];
+    fwht_row128_x16(u, sg, rot, j, y);
+    u32x2 c = {0u, 0u};
+    if (sc > 0.f) {
+      c[0] = e4m3x4_sat(y[0] / sc, y[1] / sc, y[2] / sc, y[3] / sc);
+      c[1] = e4m3x4_sat(y[4] / sc, y[5] / sc, y[6] / sc, y[7] / sc);
+    }
+    if (r < r1) reinterpret_cast<u32x2*>(X8h + (size_t)r * 128)[j] = c;
+  }
+}
+
 // ------------------------------------------------------------ quantised tiles
 struct Q8Cfg {
   static constexpr int D = 128, BM = 128, BN = 64, NT = 256;
@@ -238,6 +328,27 @@ __device__ __forceinline__ void qk_tile_i8(const char* lk, const i32x4* qop, int
     for (int kk = 0; kk < Q8Cfg::KSTEPS; ++kk) {
       const i32x4 a = lds_load<i32x4>(lk, (32 * nb + l32) * Q8Cfg::KSTRIDE + 32 * kk + 16 * h);
       acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[kk], acc[nb], 0, 0, 0);
+    }
+  }
+}
+
+// fp32 S^T for the 64 keys of the E4M3 K8 tile in LDS and the lane's E4M3
+// query: each fp8 step contracts 64 of d, its operands being two int8-form
+// 32-wide chunks side by side (A and B paired byte for byte, so every d is
+// matched with itself); products are exact, sums fp32.
+__device__ __forceinline__ void qk_tile_f8(const char* lk, const i32x4* qop, int l32, int h, f32x16* acc) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    acc[nb] = f32x16{};
+#pragma unroll
+    for (int j = 0; j < Q8Cfg::KSTEPS / 2; ++j) {
+      const int rowoff = (32 * nb + l32) * Q8Cfg::KSTRIDE + 64 * j + 16 * h;
+      const i32x4 a0 = lds_load<i32x4>(lk, rowoff);
+      const i32x4 a1 = lds_load<i32x4>(lk, rowoff + 32);
+      const i32x4 b0 = qop[2 * j], b1 = qop[2 * j + 1];
+      const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[nb], 0, 0, 0, 127, 0, 127);
     }
   }
 }
@@ -282,19 +393,28 @@ __device__ __forceinline__ uint32_t p_u8x4(float a, float b, float c, float d) {
   return x0 | (x1 << 8) | (x2 << 16) | (x3 << 24);
 }
 
+// VAR (QVariant): kInt8Scores -- int8 scores, E4M3 P . V; kAllInt8 -- I8V
+// below; kFp8 -- E4M3 Q8/K8 and the scores on the fp8 MFMA, P . V as in
+// kInt8Scores.
+// Every variant raises the running max on every increase (no lazy
+// threshold), so P = exp2(s - m_running) <= 1 when it is quantised and the
+// row's largest probability is cast as exactly 1; a lazy threshold would cast
+// P * 2^delta for a fractional delta and put up to half an E4M3 step of error
+// on the dominant key of a peaked row.
 // I8V: the all-INT8 variant -- V8 holds per-tensor int8 codes and P . V runs
-// on the int8 MFMA: P is quantised as rint(127 P), which needs P <= 1, so the
-// running max is raised on every increase (no lazy threshold); each 64-key
-// tile is two 32-key int8 steps whose operands are the two halves of the
-// E4M3 form's (same key order), and the exact int32 tile product is added
-// into the fp32 accumulator (a float rescale of an int32 running sum would
-// not be exact).
-template <bool CAUSAL, bool I8V>
+// on the int8 MFMA: P is quantised as rint(127 P) (P <= 1 as above); each
+// 64-key tile is two 32-key int8 steps whose operands are the two halves of
+// the E4M3 form's (same key order), and the exact int32 tile product is
+// added into the fp32 accumulator (a float rescale of an int32 running sum
+// would not be exact).
+template <bool CAUSAL, int VAR>
 __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
     const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, float c, int nqb, int total) {
   using C = Q8Cfg;
+  constexpr bool I8V = VAR == (int)QVariant::kAllInt8;
+  constexpr bool F8QK = VAR == (int)QVariant::kFp8;
   __shared__ __attribute__((aligned(16))) char smem[C::KBYTES + C::VBYTES];
   __shared__ __attribute__((aligned(16))) float lks[C::BN];
   char* lk = smem;
@@ -340,16 +460,24 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
     const int kv0 = t * C::BN;
     const bool skip = CAUSAL && (kv0 > qmin_w + 31 + off);
     if (!skip) {
-      i32x16 acc[2];
-      qk_tile_i8(lk, qop, l32, h, acc);
       f32x16 s[2];
+      if constexpr (F8QK) {
+        qk_tile_f8(lk, qop, l32, h, s);
+      } else {
+        i32x16 acc[2];
+        qk_tile_i8(lk, qop, l32, h, acc);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[nb][i] = (float)acc[nb][i];
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 ks4 = lds_load<f32x4>(reinterpret_cast<const char*>(lks), (32 * nb + 8 * g + 4 * h) * 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[nb][4 * g + j] = (float)acc[nb][4 * g + j] * ks4[j];
+          for (int j = 0; j < 4; ++j) s[nb][4 * g + j] *= ks4[j];
         }
       const bool need_mask = (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
       if (need_mask) {
@@ -368,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
       mt = pair_max(mt) * cq;
-      if (__any(mt > m_run + (I8V ? 0.f : kRescaleThresholdQ))) {
+      if (__any(mt > m_run)) {
         const float mn = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
@@ -401,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
           a[2 * r] = x[0];
           a[2 * r + 1] = x[1];
         }
-        if (I8V) {
+        if constexpr (I8V) {
           i32x16 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[0], a[1], a[2], a[3]},
                                                              i32x4{pb[0], pb[1], pb[2], pb[3]}, i32x16{}, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[4], a[5], a[6], a[7]}, i32x4{pb[4], pb[5], pb[6], pb[7]},
@@ -439,9 +567,12 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
   }
 }
 
-// Test hook: the exact int32 scores of one head through qk_tile_i8.
-__global__ __launch_bounds__(256) void debug_qk_i32_kernel(const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8,
-                                                           int32_t* __restrict__ S, int Nq, int Nk) {
+// Test hooks: the scores of one head through the kernels' own tile routines,
+// exact int32 through qk_tile_i8 (F8 false) or fp32 through qk_tile_f8 on
+// E4M3 codes (F8 true).
+template <bool F8>
+__global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8,
+                                                       void* __restrict__ Sv, int Nq, int Nk) {
   using C = Q8Cfg;
   __shared__ __attribute__((aligned(16))) char lk[C::KBYTES];
   const int q0 = blockIdx.x * C::BM, kv0 = blockIdx.y * C::BN;
@@ -454,8 +585,14 @@ __global__ __launch_bounds__(256) void debug_qk_i32_kernel(const int8_t* __restr
   st.load(K8, nullptr, nullptr, kv0, Nk, tid, false);
   st.store(lk, nullptr, nullptr, tid, false);
   __syncthreads();
-  i32x16 acc[2];
-  qk_tile_i8(lk, qop, l32, h, acc);
+  using Acc = typename std::conditional<F8, f32x16, i32x16>::type;
+  using Out = typename std::conditional<F8, float, int32_t>::type;
+  Acc acc[2];
+  if constexpr (F8)
+    qk_tile_f8(lk, qop, l32, h, acc);
+  else
+    qk_tile_i8(lk, qop, l32, h, acc);
+  Out* S = static_cast<Out*>(Sv);
   if (qrow < Nq) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
@@ -500,22 +637,40 @@ hipError_t launch_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_q8(const int8_t* q8, const int8_t* k8, const uint8_t* v8, const float* q_scale,
+hipError_t launch_prefill_q8(const void* q8v, const void* k8v, const void* v8v, const float* q_scale,
                              const float* k_scale, const float* v_scale, void* out, float* lse, int B, int H, int Nq,
-                             int Nk, int d, float scale, bool causal, bool v_int8, hipStream_t stream) {
+                             int Nk, int d, float scale, bool causal, QVariant variant, hipStream_t stream) {
   if (d != Q8Cfg::D) return hipErrorInvalidValue;
   const int nqb = (Nq + Q8Cfg::BM - 1) / Q8Cfg::BM;
   const int total = nqb * B * H;
-#define ATTN_Q8(CA_, I8_)                                                                                      \
-  if (causal == CA_ && v_int8 == I8_)                                                                          \
-    hipLaunchKernelGGL((prefill_q8_kernel<CA_, I8_>), dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8,     \
+  const int8_t* q8 = static_cast<const int8_t*>(q8v);
+  const int8_t* k8 = static_cast<const int8_t*>(k8v);
+  const uint8_t* v8 = static_cast<const uint8_t*>(v8v);
+  const int var = (int)variant;
+#define ATTN_Q8(CA_, VAR_)                                                                                     \
+  if (causal == CA_ && var == VAR_)                                                                            \
+    hipLaunchKernelGGL((prefill_q8_kernel<CA_, VAR_>), dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8,    \
                        q_scale, k_scale, v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb, \
                        total);
-  ATTN_Q8(true, false)
-  ATTN_Q8(false, false)
-  ATTN_Q8(true, true)
-  ATTN_Q8(false, true)
+  ATTN_Q8(true, 0)
+  ATTN_Q8(false, 0)
+  ATTN_Q8(true, 1)
+  ATTN_Q8(false, 1)
+  ATTN_Q8(true, 2)
+  ATTN_Q8(false, 2)
 #undef ATTN_Q8
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_quantize_e4m3(const void* x, const float* signs, uint8_t* x8, float* scales, int BH, int N,
+                                       int d, int block_rows, hipStream_t stream) {
+  if (d != 128 || BH < 1 || N < 1 || block_rows < 1) return hipErrorInvalidValue;
+  const int R = min(block_rows, N);
+  const int nblk = (N + R - 1) / R;
+  if ((long)BH * nblk > 0x7fffffffL) return hipErrorInvalidValue;
+  const float post = (float)(1.0 / std::sqrt((double)d));
+  hipLaunchKernelGGL(rotate_quantize_e4m3_kernel, dim3(BH * nblk), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), signs, x8, scales, N, R, nblk, post);
   return hipGetLastError();
 }
 
@@ -533,11 +688,16 @@ hipError_t launch_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out
   return hipGetLastError();
 }
 
-hipError_t launch_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d,
-                               hipStream_t stream) {
+hipError_t launch_debug_qk(const void* q8, const void* k8, void* s, int Nq, int Nk, int d, bool fp8,
+                           hipStream_t stream) {
   if (d != Q8Cfg::D) return hipErrorInvalidValue;
   dim3 grid((Nq + Q8Cfg::BM - 1) / Q8Cfg::BM, (Nk + Q8Cfg::BN - 1) / Q8Cfg::BN);
-  hipLaunchKernelGGL(debug_qk_i32_kernel, grid, dim3(256), 0, stream, q8, k8, s, Nq, Nk);
+  const int8_t* a = static_cast<const int8_t*>(q8);
+  const int8_t* b = static_cast<const int8_t*>(k8);
+  if (fp8)
+    hipLaunchKernelGGL(debug_qk_kernel<true>, grid, dim3(256), 0, stream, a, b, s, Nq, Nk);
+  else
+    hipLaunchKernelGGL(debug_qk_kernel<false>, grid, dim3(256), 0, stream, a, b, s, Nq, Nk);
   return hipGetLastError();
 }
 

@@ -272,14 +272,58 @@ int attn_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 forward with rotated, block-quantised Q and K: the incoherent processing
+ * of FlashAttention-3 as the marketmaker.cc post "Can a full trading day of
+ * context beat one minute? Flash attention and the sequence-length question"
+ * describes it (section "FA3: Hopper mechanisms", FP8 with incoherent
+ * processing).  Scores S = decode(q8) decode(k8)^T * q_scale[i] * k_scale[j]
+ * * scale on the fp8 MFMA (exact products, fp32 sums); P cast to E4M3 and
+ * P.V on the fp8 MFMA with V per-tensor E4M3, as attn_fwd_q8.
+ *   q8 [B,H,Nq,d], k8, v8 [B,H,Nk,d] E4M3 codes (uint8); q_scale [B,H,Nq],
+ *   k_scale [B,H,Nk] per-row fp32 scales (attn_rotate_quantize_e4m3 gives
+ *   them block-constant); v_scale DEVICE pointer to one float32
+ *   (attn_quantize_tensor_e4m3); out, lse, d, causal and errors as
+ *   attn_fwd_q8.  Q8 and K8 rotated by the same R give the attention of the
+ *   unrotated Q and K, since R is orthogonal.
+ */
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                 const float* q_scale, const float* k_scale, const float* v_scale,
+                 void* out, float* lse, int B, int H, int Nq, int Nk, int d,
+                 float scale, int causal, void* stream);
+
+/*
+ * Rotation and block E4M3 quantisation of Q or K for attn_fwd_fp8 (same
+ * source as attn_fwd_fp8).  x [BH, N, d] bf16, d = 128.  With signs (DEVICE,
+ * d float32 values, each +1 or -1; the caller draws them once and uses the
+ * same signs for Q and K) each row becomes y = (x * signs) H_d, H_d the
+ * Sylvester Hadamard matrix, evaluated in fp32 by butterflies at strides 1,
+ * 2, ..., d/2; signs == NULL leaves rows unrotated (y = x).  Rows are grouped
+ * per head into blocks of block_rows (the last block of a head may be
+ * shorter); a block's s = max|y| / 448 (IEEE fp32), its codes
+ * E4M3(y / s) (round to nearest even, saturating), and every row of the block
+ * gets scales[row] = s / sqrt(d) rounded to fp32 when rotated (the
+ * orthogonal rotation's normalisation), s when not; an all-zero block gives
+ * scale 0 and codes 0.  x8 [BH, N, d] uint8; scales [BH, N] float32.
+ * Errors: ATTN_E_INVALID for a NULL or misaligned pointer (x, x8 16-byte;
+ * scales, signs 4-byte) or BH, N, block_rows < 1; ATTN_E_UNSUPPORTED for
+ * d != 128.  Sign values other than +-1 are not checked.
+ */
+int attn_rotate_quantize_e4m3(const void* x, const float* signs, uint8_t* x8, float* scales,
+                              int BH, int N, int d, int block_rows, void* stream);
+
+/*
  * Test hooks that expose the quantised kernel's own device code:
  * attn_debug_qk_i32: s[i,j] = sum_t q8[i,t] k8[j,t] for one head
  *   (q8 [Nq,d], k8 [Nk,d] int8, s [Nq,Nk] int32), through the same int8
  *   MFMA tile routine as attn_fwd_q8; d == 128.
+ * attn_debug_qk_f8: s[i,j] = sum_t E4M3(q8[i,t]) E4M3(k8[j,t]) for one
+ *   head (uint8 codes, s fp32), through the same fp8 MFMA tile routine as
+ *   attn_fwd_fp8; d == 128.
  * attn_debug_cvt_e4m3: y[i] = E4M3(x[i]) through the same conversion
  *   routine attn_quantize_tensor_e4m3 uses (saturating); n even.
  */
 int attn_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d, void* stream);
+int attn_debug_qk_f8(const uint8_t* q8, const uint8_t* k8, float* s, int Nq, int Nk, int d, void* stream);
 int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream);
 
 /* Static text for a return code. */

@@ -738,19 +738,9 @@ def pin_fp8_attention(attention_fp8_head):
 
 
 def outlier_inputs(seed, N, d, kind):
-    """Synthetic Q, K, V (fp32 values of bf16) with outliers: 'sparse' puts
-    0.1 % of the entries of each tensor at N(0, 10); 'channel' multiplies four
-    fixed channels of Q and K by 10 (the same channels for every token)."""
+    """fp32 values of the bf16 Q, K, V drawn by fa_inputs.outlier_qkv."""
     import fa_inputs as G
-    rng = np.random.default_rng(seed)
-    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
-    if kind == "sparse":
-        q, k, v = (np.where(rng.random(x.shape) < 1e-3, rng.standard_normal(x.shape) * 10, x) for x in (q, k, v))
-    elif kind == "channel":
-        ch = rng.choice(d, 4, replace=False)
-        q[:, ch] *= 10
-        k[:, ch] *= 10
-    return tuple(G.to_f32(G.round_to_bf16_bits(x.astype(np.float32)), "bf16") for x in (q, k, v))
+    return tuple(G.to_f32(x, "bf16") for x in G.outlier_qkv(seed, N, d, kind))
 
 
 def pin_rotation_lowers_error(attention_rotated_fp8):

@@ -121,7 +121,30 @@ def test_quant_entry_points_reject():
     assert L.attn_quantize_tensor_i8(MIS, A, A, 1 << 20, A, 1 << 20, None) == Bd.ATTN_E_INVALID
     assert L.attn_quantize_tensor_i8(A, A, A, 1 << 20, A, 4, None) == Bd.ATTN_E_WORKSPACE
     assert L.attn_quantize_tensor_i8(A, A, A, 1 << 20, None, 1 << 20, None) == Bd.ATTN_E_WORKSPACE
+    f8 = lambda **kw: L.attn_fwd_fp8(kw.get("q", A), A, A, A, kw.get("ks", A), kw.get("vs", A), A, A,
+                                     1, 1, kw.get("Nq", 8), 8, kw.get("d", 128), kw.get("scale", 0.1),
+                                     kw.get("causal", 0), None)
+    assert f8(d=64) == Bd.ATTN_E_UNSUPPORTED
+    assert f8(ks=None) == Bd.ATTN_E_INVALID
+    assert f8(vs=A + 2) == Bd.ATTN_E_INVALID
+    assert f8(q=MIS) == Bd.ATTN_E_INVALID
+    assert f8(Nq=9, causal=1) == Bd.ATTN_E_INVALID
+    assert f8(scale=float("nan")) == Bd.ATTN_E_INVALID
+    rq = lambda **kw: L.attn_rotate_quantize_e4m3(kw.get("x", A), kw.get("signs", A), A, kw.get("sc", A),
+                                                  kw.get("BH", 2), kw.get("N", 64), kw.get("d", 128),
+                                                  kw.get("blk", 64), None)
+    assert rq(d=64) == Bd.ATTN_E_UNSUPPORTED
+    assert rq(signs=None, d=96) == Bd.ATTN_E_UNSUPPORTED
+    assert rq(x=None) == Bd.ATTN_E_INVALID
+    assert rq(x=MIS) == Bd.ATTN_E_INVALID
+    assert rq(signs=A + 2) == Bd.ATTN_E_INVALID
+    assert rq(sc=None) == Bd.ATTN_E_INVALID
+    assert rq(BH=0) == Bd.ATTN_E_INVALID
+    assert rq(N=0) == Bd.ATTN_E_INVALID
+    assert rq(blk=0) == Bd.ATTN_E_INVALID
     assert L.attn_debug_qk_i32(A, A, A, 4, 4, 64, None) == Bd.ATTN_E_UNSUPPORTED
+    assert L.attn_debug_qk_f8(A, A, A, 4, 4, 64, None) == Bd.ATTN_E_UNSUPPORTED
+    assert L.attn_debug_qk_f8(A, None, A, 4, 4, 128, None) == Bd.ATTN_E_INVALID
     assert L.attn_debug_qk_i32(None, A, A, 4, 4, 128, None) == Bd.ATTN_E_INVALID
     assert L.attn_debug_cvt_e4m3(A, A, 3, None) == Bd.ATTN_E_INVALID
 

@@ -268,3 +268,167 @@ def test_i8_full_size_sampled(F):
                 assert np.abs(l_all[b, h, rows] - L).max() <= LSE_TOL
         print(f"  sampled max|dO|={worst:.3e}", flush=True)
         assert worst <= QO_TOL
+
+
+# ---- rotated FP8: random-sign Hadamard rotation + block E4M3 of Q and K -----
+
+from oracle import rotated as RT  # noqa: E402
+
+
+def _signs_dev(d=128, seed=90):
+    import torch
+    s = G.draw_signs(seed, d)
+    return s, torch.from_numpy(s).cuda()
+
+
+@pytest.mark.parametrize("N,block_rows,rotate", [(1, 64, True), (64, 64, True), (150, 64, True), (333, 100, True),
+                                                (200, 1, True), (130, 1000, True), (150, 64, False),
+                                                (77, 16, False)],
+                         ids=lambda x: str(x))
+def test_rotate_quantize_bit_exact(F, N, block_rows, rotate):
+    """Codes and per-row scales equal the oracle's emulation bit for bit
+    (the fp32 transform in the same butterfly order decides every code),
+    with short last blocks, a zero block and rows of mixed magnitude."""
+    import torch
+    from tests.gpu_util import to_dev
+    rng = np.random.default_rng(91 + N)
+    x = (rng.standard_normal((2, 3, N, 128)) * rng.uniform(0.1, 8, (2, 3, N, 1))).astype(np.float32)
+    x[0, 1, :min(N, block_rows)] = 0.0                    # one all-zero block
+    bits = G.round_to_bf16_bits(x)
+    s_np, s_dev = _signs_dev()
+    sg = s_np if rotate else None
+    print(f"  gpu: rotate_quantize_e4m3 N={N} block_rows={block_rows} rotate={rotate}", flush=True)
+    x8, sc = F.rotate_quantize_e4m3(to_dev(bits, "bf16"), s_dev if rotate else None, block_rows)
+    torch.cuda.synchronize()
+    c_ref, s_ref = RT.rotate_quantize_e4m3(G.to_f32(bits, "bf16"), sg, block_rows)
+    got_c, got_s = x8.cpu().numpy(), sc.cpu().numpy()
+    bad = np.argwhere(got_c != c_ref)
+    assert bad.size == 0, (bad[:5], got_c[tuple(bad[0])], c_ref[tuple(bad[0])])
+    assert np.array_equal(got_s, s_ref)
+
+
+def _fp8_case(F, q, k, v, signs_np, signs_dev, block_rows=64):
+    import torch
+    from tests.gpu_util import to_dev
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    q8, sq = F.rotate_quantize_e4m3(tq, signs_dev, block_rows)
+    k8, sk = F.rotate_quantize_e4m3(tk, signs_dev, block_rows)
+    v8, sv = F.quantize_tensor_e4m3(tv)
+    torch.cuda.synchronize()
+    return q8, sq, k8, sk, v8, sv
+
+
+@pytest.mark.parametrize("shape,causal,rotate", [((1, 2, 300, 300), False, True), ((2, 1, 77, 333), True, True),
+                                                 ((1, 1, 128, 64), False, True), ((1, 2, 200, 1000), False, True),
+                                                 ((1, 1, 260, 260), True, True), ((1, 1, 1, 1), False, True),
+                                                 ((1, 2, 300, 300), False, False)],
+                         ids=lambda x: str(x))
+def test_fp8_small(F, shape, causal, rotate):
+    import torch
+    from tests.gpu_util import errors, from_dev
+    B, H, Nq, Nk = shape
+    w = G.Workload("fp8_small", 92, B, H, Nq, Nk, 128, "bf16", 1.0, causal, 128 ** -0.5)
+    q, k, v = G.draw_qkv(w)
+    s_np, s_dev = _signs_dev()
+    sg, sd = (s_np, s_dev) if rotate else (None, None)
+    f32 = lambda x: G.to_f32(x, "bf16")
+    O, L, qi = RT.attention_rotated_fp8(f32(q), f32(k), f32(v), sg, w.scale, causal, 64)
+    q8, sq, k8, sk, v8, sv = _fp8_case(F, q, k, v, sg, sd)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    print(f"  gpu: attn_fwd_fp8 {shape} causal={causal} rotate={rotate}", flush=True)
+    out, lse = F.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    eo, ro = errors(from_dev(out), O)
+    el, _ = errors(from_dev(lse), L)
+    print(f"  max|dO|={eo:.3e} (rel {ro:.3e}) max|dLSE|={el:.3e}", flush=True)
+    assert eo <= QO_TOL and el <= LSE_TOL
+
+
+def test_fp8_score_accumulation_precision(F):
+    """The fp8 MFMA tile's fp32 scores against the exact sums of the E4M3
+    products: the matrix cores add the products of a step with less than
+    fp32 precision (measured worst case 2^-11.9 of sum |products| with
+    outlier channels left unrotated, about 2^-16 otherwise); the bounds
+    below are twice those."""
+    import torch
+    f32 = lambda x: G.to_f32(x, "bf16")
+    for kind, rotate, bound in (("none", True, 2.0 ** -15), ("channel", True, 2.0 ** -15),
+                                ("channel", False, 2.0 ** -11), ("sparse", False, 2.0 ** -13)):
+        q, k, _ = G.outlier_qkv(74, 256, 128, kind)
+        sg = G.draw_signs(90, 128) if rotate else None
+        q8, _ = RT.rotate_quantize_e4m3(f32(q), sg, 64)
+        k8, _ = RT.rotate_quantize_e4m3(f32(k), sg, 64)
+        print(f"  gpu: debug_qk_f8 {kind} rotate={rotate}", flush=True)
+        s = F.debug_qk_f8(torch.from_numpy(q8).cuda(), torch.from_numpy(k8).cuda())
+        torch.cuda.synchronize()
+        a, b = Q.e4m3_decode(q8), Q.e4m3_decode(k8)
+        rel = np.abs(s.cpu().numpy() - a @ b.T) / np.maximum(np.abs(a) @ np.abs(b).T, 1e-30)
+        print(f"  max err / sum|products| = 2^{np.log2(rel.max() + 1e-300):.1f}", flush=True)
+        assert rel.max() <= bound
+
+
+def test_fp8_rotation_lowers_error(F):
+    """The method's claim on the GPU path: with outliers in shared channels
+    of Q and K, rotating before block quantisation lowers the error of the
+    FP8 forward against the exact fp64 definition (the oracle measures 3.1x
+    on these inputs).  On these peaked rows the method's own error is far
+    above the quantised tolerance (max |O - O_exact| near 1), so each GPU
+    result is held to its oracle's accuracy instead: its RMSE against the
+    exact definition is within 25 % of the oracle's."""
+    import torch
+    from oracle import attention as Am
+    from tests.gpu_util import from_dev
+    N, d = 256, 128
+    q, k, v = G.outlier_qkv(74, N, d, "channel")
+    f32 = lambda x: G.to_f32(x, "bf16")
+    O, _ = Am.attention_head(f32(q).astype(np.float64), f32(k).astype(np.float64), f32(v).astype(np.float64),
+                             d ** -0.5)
+    s_np, s_dev = _signs_dev()
+    rmse = []
+    for sg, sd in ((None, None), (s_np, s_dev)):
+        q8, sq, k8, sk, v8, sv = _fp8_case(F, q[None, None], k[None, None], v[None, None], sg, sd)
+        out, _ = F.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, scale=d ** -0.5)
+        torch.cuda.synchronize()
+        o = from_dev(out)[0, 0]
+        Oq, _, _ = RT.attention_rotated_fp8(f32(q), f32(k), f32(v), sg, d ** -0.5, False, 64)
+        e_gpu = np.sqrt(np.mean((o - O) ** 2))
+        e_orc = np.sqrt(np.mean((Oq - O) ** 2))
+        print(f"  rotate={sg is not None}: rmse vs exact gpu {e_gpu:.3e} oracle {e_orc:.3e}; "
+              f"max |gpu - oracle| {np.abs(o - Oq).max():.3e}", flush=True)
+        assert e_gpu <= 1.25 * e_orc
+        rmse.append(e_gpu)
+    print(f"  ratio unrotated / rotated {rmse[0] / rmse[1]:.2f}", flush=True)
+    assert rmse[0] / rmse[1] >= 2.0
+
+
+def test_fp8_full_size_sampled(F):
+    """B=2 H=32 N=8192 d=128 rotated FP8: quantisation bit-exact, sampled
+    rows of sampled heads against the oracle, both masks."""
+    import torch
+    from tests.gpu_util import from_dev
+    w = G.WORKLOADS["quant_8k"]
+    q, k, v = G.draw_qkv(w, threads=16)
+    f32 = lambda x: G.to_f32(x, "bf16")
+    s_np, s_dev = _signs_dev()
+    qi = RT.quantize_inputs(f32(q), f32(k), f32(v), s_np, 64)
+    q8, sq, k8, sk, v8, sv = _fp8_case(F, q, k, v, s_np, s_dev)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    for causal in (False, True):
+        print(f"  gpu: attn_fwd_fp8 full size causal={causal}", flush=True)
+        out, lse = F.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        o_all, l_all = from_dev(out), from_dev(lse)
+        assert np.isfinite(o_all).all() and np.isfinite(l_all).all()
+        rng = np.random.default_rng(5)
+        worst = 0.0
+        for bh in rng.choice(w.B * w.H, 4, replace=False):
+            b, h = divmod(int(bh), w.H)
+            rows = np.unique(np.concatenate([[0, 8191], rng.integers(0, w.Nq, 32)]))
+            for r in rows:
+                nk = r + 1 if causal else w.Nk
+                O, L = RT.attention_fp8_head(qi["q8"][b, h][r:r + 1], qi["sq"][b, h][r:r + 1], qi["k8"][b, h][:nk],
+                                             qi["sk"][b, h][:nk], qi["v8"][b, h][:nk], qi["sv"], w.scale)
+                worst = max(worst, np.abs(o_all[b, h, r] - O[0]).max())
+                assert abs(l_all[b, h, r] - L[0]) <= LSE_TOL
+        print(f"  sampled max|dO|={worst:.3e}", flush=True)
+        assert worst <= QO_TOL
