@@ -305,8 +305,18 @@ struct Q8Cfg {
   static constexpr int MB_O = D / 32;
 };
 
-// Row of the V8 tile in LDS for tile key kt = 8a + 4h + b: 32h + 4a + b.
-__device__ __forceinline__ int v8_lds_row(int kt) { return ((kt >> 2) & 1) * 32 + (kt >> 3) * 4 + (kt & 3); }
+// Key order of a score tile.  The K8 tile is staged so that row 8g + 4h + r
+// of score block nb holds tile key 32h + 16nb + 4g + r: score s[nb][i] of a
+// lane in half h is then key 32h + 16nb + i, i.e. each lane half holds the 32
+// consecutive keys 32h .. 32h+31 (one scale block of the fp4 P operand).  P^T
+// byte (or nibble) j of lane half h is key 32h + j, which is the V row the
+// transposing V^T read of that half returns at position j, so V rows are
+// staged in key order.
+__device__ __forceinline__ int k8_lds_row(int kt) {
+  const int h = kt >> 5, nb = (kt >> 4) & 1, g = (kt >> 2) & 3, r = kt & 3;
+  return 32 * nb + 8 * g + 4 * h + r;
+}
+__device__ __forceinline__ int score_key(int nb, int i, int h) { return 32 * h + 16 * nb + i; }
 
 // B operand of S^T = K8 Q8^T: lane holds Q8[qrow][32kk + 16h .. +15].
 __device__ __forceinline__ void load_q8_operand(const int8_t* Q8row, bool valid, int h, i32x4* qop) {
@@ -319,7 +329,8 @@ __device__ __forceinline__ void load_q8_operand(const int8_t* Q8row, bool valid,
 }
 
 // Exact int32 S^T for the 64 keys of the K8 tile in LDS and the lane's query:
-// acc[nb][i] = sum_t K8[32nb + 8(i/4) + 4h + i%4][t] * Q8[q][t].
+// acc[nb][i] = sum_t K8[LDS row 32nb + 8(i/4) + 4h + i%4][t] * Q8[q][t], i.e.
+// the score of tile key score_key(nb, i, h).
 __device__ __forceinline__ void qk_tile_i8(const char* lk, const i32x4* qop, int l32, int h, i32x16* acc) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -378,8 +389,8 @@ struct Q8Stage {
 #pragma unroll
     for (int p = 0; p < Q8Cfg::PASSES; ++p) {
       const int row = p * Q8Cfg::RPP + tid / Q8Cfg::CPR, ch = tid % Q8Cfg::CPR;
-      lds_store<u32x4>(lk, row * Q8Cfg::KSTRIDE + ch * 16, k[p]);
-      if (with_v) lds_store<u32x4>(lv, v8_lds_row(row) * Q8Cfg::VSTRIDE + ch * 16, v[p]);
+      lds_store<u32x4>(lk, k8_lds_row(row) * Q8Cfg::KSTRIDE + ch * 16, k[p]);
+      if (with_v) lds_store<u32x4>(lv, row * Q8Cfg::VSTRIDE + ch * 16, v[p]);
     }
     if (lks != nullptr && tid < Q8Cfg::BN) lks[tid] = ks;
   }
@@ -475,7 +486,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 ks4 = lds_load<f32x4>(reinterpret_cast<const char*>(lks), (32 * nb + 8 * g + 4 * h) * 4);
+          const f32x4 ks4 = lds_load<f32x4>(reinterpret_cast<const char*>(lks), score_key(nb, 4 * g, h) * 4);
 #pragma unroll
           for (int j = 0; j < 4; ++j) s[nb][4 * g + j] *= ks4[j];
         }
@@ -486,7 +497,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
+            const int key = kv0 + score_key(nb, i, h);
             if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
           }
       }
@@ -598,7 +609,7 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
+        const int key = kv0 + score_key(nb, i, h);
         if (key < Nk) S[(size_t)qrow * Nk + key] = acc[nb][i];
       }
   }
