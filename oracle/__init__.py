@@ -22,6 +22,8 @@ Sources, cited by short name in the modules:
                   attention kernels still dominate".
   [INT-FA post]   "INT-FlashAttention: an INT8 quantisation architecture
                   compatible with FlashAttention" (hoodcat.net, Spanish).
+  [FP4 summary]   summary of "Hardware-Aware FP4 FlashAttention-4"
+                  (gist.science, Chinese) -- summary and explainer.
 
 Modules:
   attention   -- the plain definition (two-pass softmax, fp64).
@@ -37,7 +39,9 @@ Modules:
   rotated     -- FP8 attention with Q and K rotated by a random-sign Hadamard
                  matrix before block quantisation ([trading post], "FA3:
                  Hopper mechanisms", FP8 with incoherent processing).
+  fp4         -- the same FP8 attention with P in MXFP4 (E2M1 codes, one
+                 power-of-two scale per 32 keys of a row) ([FP4 summary]).
 
 Parity status of every function is stated in its module header.
 """
-from . import attention, backward, quant, recurrence, rotated, variants  # noqa: F401
+from . import attention, backward, fp4, quant, recurrence, rotated, variants  # noqa: F401

@@ -761,3 +761,116 @@ def pin_rotation_lowers_error(attention_rotated_fp8):
             o, _, _ = attention_rotated_fp8(q, k, v, sg, d ** -0.5, False, 64)
             e.append(np.sqrt(np.mean((o - O) ** 2)))
         assert lo <= e[0] / e[1] <= hi, (kind, e)
+
+
+# ---- FP8 attention with P in MXFP4
+
+def pin_e2m1(encode, decode):
+    """E2M1 from the format's definition: (-1)^s 2^(e-1) (1 + m/2) for e > 0
+    and (-1)^s m/2 for e = 0; encoding maps each value to its code, each
+    midpoint to the even neighbour, anything just off a midpoint to the
+    nearer value, and saturates at 6."""
+    vals = []
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        v = (0.5 * m) if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+        vals.append(-v if s else v)
+    assert np.array_equal(decode(np.arange(16)), np.array(vals))
+    pos = np.array(vals[:8])
+    assert np.array_equal(encode(pos), np.arange(8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    want = np.array([0, 2, 2, 4, 4, 6, 6])              # ties to the even code
+    assert np.array_equal(encode(mids), want)
+    assert np.array_equal(encode(np.nextafter(mids, np.inf)), np.arange(1, 8))
+    assert np.array_equal(encode(np.nextafter(mids, -np.inf)), np.arange(0, 7))
+    assert np.array_equal(encode(np.array([6.0, 6.5, 7.0, 7.9, 100.0])), [7, 7, 7, 7, 7])
+    assert np.array_equal(encode(-pos[1:]), np.arange(9, 16))
+
+
+def pin_mx_p(quantize_p_mx, encode, decode):
+    """(a) Powers of two at or above 1/8 of their block's max are exact, at or
+    below 1/16 of it they vanish (1/16 is a tie to 0); (b) blocks are 32
+    consecutive keys from key 0 (a short last block included), each with
+    its own scale; (c) every element equals the brute-force nearest of the
+    eight scaled codes (ties to even) under the block's scale."""
+    p = np.zeros((2, 70))
+    p[0, :32] = 2.0 ** -np.arange(32)           # block max 1
+    p[0, 32:64] = 3.0 * 2.0 ** -np.arange(32)   # block max 3 (not a power of two)
+    p[0, 64:] = 0.01
+    p[1, 5] = 0.2
+    out = quantize_p_mx(p)
+    assert np.array_equal(out[0, :4], p[0, :4]) and np.all(out[0, 4:32] == 0)
+    # block max 3: e = floor(log2 3) - 2 = -1, y = 6 * 2^-k: 6, 3, 1.5, 0.75 -> 1, 0.375 -> 0.5, then 0.1875 -> 0
+    assert np.array_equal(out[0, 32:39], np.array([6, 3, 1.5, 1, 0.5, 0, 0]) * 0.5)
+    # a short block of 0.01: e = floor(log2 0.01) - 2 = -9, y = 5.12 -> 6
+    assert np.all(out[0, 64:] == 6 * 2.0 ** -9)
+    # a lone 0.2: e = -5, y = 6.4 saturates to 6
+    assert np.all(out[1, np.arange(70) != 5] == 0) and out[1, 5] == 6 * 2.0 ** -5
+    rng = np.random.default_rng(75)
+    p = rng.random((5, 100)) ** 4
+    out = quantize_p_mx(p)
+    grid = decode(np.arange(8))
+    for r in range(5):
+        for b0 in range(0, 100, 32):
+            blk = p[r, b0:b0 + 32]
+            e = np.floor(np.log2(blk.max())) - 2
+            y = blk / 2.0 ** e
+            d = np.abs(y[:, None] - grid[None, :])
+            best = d.min(axis=1, keepdims=True)
+            cand = np.where(d == best, np.arange(8)[None, :], 99)
+            even = np.where(cand % 2 == 0, cand, 99).min(axis=1)
+            pick = np.where(even < 99, even, cand.min(axis=1))
+            pick = np.where(y >= 6, 7, pick)
+            assert np.array_equal(out[r, b0:b0 + 32], grid[pick] * 2.0 ** e)
+
+
+def pin_fp4p_attention(attention_fp4p_head, attention_fp8_head):
+    """(a) Zero query codes: every P is 1, cast exactly (4 in the top
+    binade): O = mean of the dequantised V, LSE = ln Nk; (b) one dominant key
+    j per row, every other P = x = e^-16: the keys sharing j's block are cast
+    to 0 (below 1/16 of its P), every other block of equal x to c(x) = 4 or
+    6 times its scale (x / 2^e in [4, 8): 4 up to the tie at 5, else 6), so
+    O = (V_j + c(x) * sum of V outside j's block) / l; (c)
+    where every P is a power of two no smaller than 1/8 of its block's max,
+    both formats are exact and the attention equals the FP8 oracle's."""
+    from oracle import quant as Qm
+    rng = np.random.default_rng(76)
+    Nk, d = 70, 16
+    vc = Qm.e4m3_encode(rng.standard_normal((Nk, d)) * 100)
+    sv = np.float32(0.02)
+    vd = Qm.e4m3_decode(vc) * float(sv)
+    kc = Qm.e4m3_encode(rng.standard_normal((Nk, d)) * 50)
+    sk = np.full(Nk, 0.01, np.float32)
+    o, l = attention_fp4p_head(np.zeros((3, d), np.uint8), np.full(3, 0.01, np.float32), kc, sk, vc, sv, 0.3)
+    assert np.allclose(o, vd.mean(axis=0)[None], atol=1e-12) and np.allclose(l, np.log(Nk), atol=1e-12)
+    # (b) q . k_j large for one key per row: integer codes, score gap >= 8 (P <= e^-8 < 1/16)
+    qi = np.zeros((4, d))
+    ki = np.zeros((Nk, d))
+    for r in range(4):
+        qi[r, r] = 16
+        ki[7 * r + 3, r] = 16
+    qc, kc2 = Qm.e4m3_encode(qi), Qm.e4m3_encode(ki)
+    ones = np.ones(4, np.float32)
+    o, lse = attention_fp4p_head(qc, ones, kc2, np.ones(Nk, np.float32), vc, sv, 1 / 16.0)
+    x = np.exp(-16.0)
+    e = np.floor(np.log2(x)) - 2
+    cx = (4.0 if x / 2.0 ** e <= 5 else 6.0) * 2.0 ** e
+    l_r = 1 + (Nk - 1) * x
+    for r in range(4):
+        j = 7 * r + 3
+        others = np.ones(Nk, bool)
+        others[(j // 32) * 32:(j // 32) * 32 + 32] = False
+        want = (vd[j] + cx * vd[others].sum(axis=0)) / l_r
+        assert np.allclose(o[r], want, atol=1e-12, rtol=0)
+        assert abs(lse[r] - (16 + np.log(l_r))) < 1e-12
+    # (c) scores -k ln 2 (k = 0 .. 3) in every block: q = 1 on channel 0, k_j = -(j % 4)
+    qi = np.zeros((2, d))
+    qi[:, 0] = 1
+    ki = np.zeros((Nk, d))
+    ki[:, 0] = -(np.arange(Nk) % 4)
+    ones_k = np.ones(Nk, np.float32)
+    a = attention_fp4p_head(Qm.e4m3_encode(qi), np.ones(2, np.float32), Qm.e4m3_encode(ki), ones_k, vc, sv,
+                            float(np.log(2.0)))
+    b = attention_fp8_head(Qm.e4m3_encode(qi), np.ones(2, np.float32), Qm.e4m3_encode(ki), ones_k, vc, sv,
+                           float(np.log(2.0)))
+    assert np.allclose(a[0], b[0], atol=1e-13, rtol=0) and np.allclose(a[1], b[1], atol=1e-13)
