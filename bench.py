@@ -18,9 +18,9 @@ Printed as ONE JSON line, which also carries
     prefill configuration (algorithmic FLOPs of its five matrix products,
     2.5x the forward's), grouped-query prefill and decode (32 query heads on
     8 K/V heads), a packed variable-length causal batch, the split-KV decode
-    (GB/s over the K+V bytes) and the three quantised forwards (int8 scores
-    with fp8 P.V, the all-INT8 form, and FP8 with rotated Q and K), each
-    timed the same way (informational).
+    (GB/s over the K+V bytes) and the four quantised forwards (int8 scores
+    with fp8 P.V, the all-INT8 form, FP8 with rotated Q and K, and the same
+    with P in MXFP4), each timed the same way (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
                        [--copy-calibration]
@@ -407,6 +407,11 @@ def main():
                                 args.steps, args.warmup)
         _, perr = timed_launches([lambda: (F.rotate_quantize_e4m3(tq, sgn, 64), F.rotate_quantize_e4m3(tk, sgn, 64))],
                                  5, 1)
+        _, per4 = timed_launches([lambda: F.attn_fwd_fp4p(f8q, f8k, v8, fsq, fsk, sv, scale=wq.scale, out=o, lse=l)],
+                                 args.steps, args.warmup)
+        other["quant_fp4p_8k"] = {"ms": round(per4[0] * 1e3, 4), "tflops": round(ops / per4[0] / 1e12, 3),
+                                  "frac_fp8_peak": round(ops / per4[0] / 1e12 / PEAK_FP8_TFLOPS, 4),
+                                  "p_format": "MXFP4 (E2M1, one E8M0 scale per 32 keys)"}
         other["quant_fp8_rotated_8k"] = {"ms": round(per[0] * 1e3, 4), "tflops": round(ops / per[0] / 1e12, 3),
                                          "frac_fp8_peak": round(ops / per[0] / 1e12 / PEAK_FP8_TFLOPS, 4),
                                          "rotate_quantize_qk_ms": round(perr[0] * 1e3, 4), "block_rows": 64}

@@ -41,6 +41,8 @@ SIGNATURES = {
     "attn_quantize_tensor_i8": (_I, [_P, _P, _P, _L, _P, _Z, _P]),
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_rotate_quantize_e4m3": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "attn_fwd_fp4p": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_debug_cvt_e2m1": (_I, [_P, _P, _L, _P]),
     "attn_debug_qk_i32": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_debug_qk_f8": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_debug_cvt_e4m3": (_I, [_P, _P, _L, _P]),
@@ -378,6 +380,23 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, sc
     return out, lse
 
 
+def attn_fwd_fp4p(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
+                  out=None, lse=None):
+    """attn_fwd_fp8 with P in MXFP4 (E2M1 codes, one power-of-two scale per 32
+    keys of a query).  Same arguments and results as attn_fwd_fp8."""
+    torch = _torch()
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
+    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
+    rc = lib().attn_fwd_fp4p(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
+                             _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
+                             B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
+    _check(rc, "attn_fwd_fp4p")
+    return out, lse
+
+
 def debug_qk_i32(q8, k8):
     """int32 Q8 K8^T of one head through the quantised kernel's tile routine."""
     torch = _torch()
@@ -398,6 +417,14 @@ def debug_qk_f8(q8, k8):
     _check(lib().attn_debug_qk_f8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(s, "s"), Nq, Nk, d, _stream()),
            "attn_debug_qk_f8")
     return s
+
+
+def debug_cvt_e2m1(x):
+    """E2M1 codes (one per byte) of an fp32 GPU tensor through the library's FP4 conversion."""
+    torch = _torch()
+    y = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
+    _check(lib().attn_debug_cvt_e2m1(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream()), "attn_debug_cvt_e2m1")
+    return y
 
 
 def debug_cvt_e4m3(x):

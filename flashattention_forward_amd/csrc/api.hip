@@ -261,6 +261,18 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const 
                                             causal != 0, attn::QVariant::kFp8, static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_fp4p(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale, const float* k_scale,
+                  const float* v_scale, void* out, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                  int causal, void* stream) {
+  int rc = check_common(q8, k8, v8, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (!q_scale || !k_scale || !v_scale || !aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale))
+    return ATTN_E_INVALID;
+  if (d != 128) return ATTN_E_UNSUPPORTED;
+  return hip_status(attn::launch_prefill_q8(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, B, H, Nq, Nk, d, scale,
+                                            causal != 0, attn::QVariant::kFp8P4, static_cast<hipStream_t>(stream)));
+}
+
 int attn_rotate_quantize_e4m3(const void* x, const float* signs, uint8_t* x8, float* scales, int BH, int N, int d,
                               int block_rows, void* stream) {
   if (!x || !x8 || !scales || BH < 1 || N < 1 || block_rows < 1) return ATTN_E_INVALID;
@@ -293,6 +305,13 @@ int attn_debug_qk_f8(const uint8_t* q8, const uint8_t* k8, float* s, int Nq, int
   if (!aligned16(q8) || !aligned16(k8) || !aligned4(s)) return ATTN_E_INVALID;
   if (d != 128) return ATTN_E_UNSUPPORTED;
   return hip_status(attn::launch_debug_qk(q8, k8, s, Nq, Nk, d, true, static_cast<hipStream_t>(stream)));
+}
+
+int attn_debug_cvt_e2m1(const float* x, uint8_t* y, long n, void* stream) {
+  if (!x || !y || n < 8 || n % 8) return ATTN_E_INVALID;
+  if (!aligned4(x)) return ATTN_E_INVALID;
+  if ((n / 8 + 255) / 256 > INT_MAX) return ATTN_E_INVALID;
+  return hip_status(attn::launch_debug_cvt_e2m1(x, y, n, static_cast<hipStream_t>(stream)));
 }
 
 int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream) {

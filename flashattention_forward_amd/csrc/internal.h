@@ -77,8 +77,10 @@ hipError_t launch_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_
 // The quantised forwards share one kernel: kInt8Scores has int8 Q8/K8 and
 // E4M3 V8 and P (int8 scores, fp8 P . V); kAllInt8 has int8 V8 and P
 // (both products on the int8 MFMA); kFp8 has E4M3 Q8/K8, V8 and P (both
-// products on the fp8 MFMA).
-enum class QVariant : int { kInt8Scores = 0, kAllInt8 = 1, kFp8 = 2 };
+// products on the fp8 MFMA); kFp8P4 is kFp8 with P in MXFP4 (E2M1 codes,
+// one power-of-two scale per 32 keys of a query; P . V on the mixed
+// fp8 x fp4 MFMA).
+enum class QVariant : int { kInt8Scores = 0, kAllInt8 = 1, kFp8 = 2, kFp8P4 = 3 };
 hipError_t launch_prefill_q8(const void* q8, const void* k8, const void* v8,
                              const float* q_scale, const float* k_scale, const float* v_scale,
                              void* out, float* lse, int B, int H, int Nq, int Nk, int d,
@@ -93,5 +95,6 @@ hipError_t launch_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out
 hipError_t launch_debug_qk(const void* q8, const void* k8, void* s, int Nq, int Nk, int d, bool fp8,
                            hipStream_t stream);
 hipError_t launch_debug_cvt_e4m3(const float* x, uint8_t* y, long n, hipStream_t stream);
+hipError_t launch_debug_cvt_e2m1(const float* x, uint8_t* y, long n, hipStream_t stream);
 
 }  // namespace attn

@@ -192,6 +192,36 @@ __global__ __launch_bounds__(256) void quantize_i8_tensor_kernel(const uint16_t*
   }
 }
 
+// E2M1 (OCP FP4) codes of two non-negative floats in one byte (first value in
+// the low nibble), through the hardware conversion (scale 1); values above
+// the largest code's 6 are clamped to it first.
+__device__ __forceinline__ uint32_t e2m1x2_into(uint32_t word, float a, float b, int byte) {
+  a = fminf(a, 6.f);
+  b = fminf(b, 6.f);
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, 3);
+  }
+}
+
+// eight values per thread packed into one dword through bytes 0 .. 3 in
+// turn, as the P operand is packed, then unpacked one code per byte
+__global__ __launch_bounds__(256) void debug_cvt_e2m1_kernel(const float* __restrict__ x, uint8_t* __restrict__ y,
+                                                             long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (8 * i + 7 < n) {
+    const float* xi = x + 8 * i;
+    uint32_t w = e2m1x2_into(0u, xi[0], xi[1], 0);
+    w = e2m1x2_into(w, xi[2], xi[3], 1);
+    w = e2m1x2_into(w, xi[4], xi[5], 2);
+    w = e2m1x2_into(w, xi[6], xi[7], 3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[8 * i + j] = (w >> (4 * j)) & 0xFu;
+  }
+}
+
 __global__ __launch_bounds__(256) void debug_cvt_e4m3_kernel(const float* __restrict__ x, uint8_t* __restrict__ y, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (2 * i + 1 < n) {
@@ -318,6 +348,16 @@ __device__ __forceinline__ int k8_lds_row(int kt) {
 }
 __device__ __forceinline__ int score_key(int nb, int i, int h) { return 32 * h + 16 * nb + i; }
 
+// The mixed fp8 x fp4 MFMA pairs its operands by K index, and the two
+// formats lay K out differently: fp4 element j of lane half h is K = 32h + j
+// (the P nibbles, key 32h + j as above), fp8 element j of lane half h is
+// K = 16h + j for j < 16 and 32 + 16h + (j - 16) for j >= 16.  For P in fp4
+// the V row of tile key kt is therefore staged at the LDS row whose
+// transposed read lands on the fp8 element with K index kt.
+__device__ __forceinline__ int v8_lds_row_p4(int kt) {
+  return kt < 32 ? 32 * (kt >> 4) + (kt & 15) : 32 * ((kt - 32) >> 4) + 16 + (kt & 15);
+}
+
 // B operand of S^T = K8 Q8^T: lane holds Q8[qrow][32kk + 16h .. +15].
 __device__ __forceinline__ void load_q8_operand(const int8_t* Q8row, bool valid, int h, i32x4* qop) {
 #pragma unroll
@@ -385,12 +425,13 @@ struct Q8Stage {
     ks = 0.f;
     if (KS != nullptr && tid < Q8Cfg::BN && kv0 + tid < Nk) ks = KS[kv0 + tid];
   }
+  template <bool P4 = false>
   __device__ __forceinline__ void store(char* lk, char* lv, float* lks, int tid, bool with_v) const {
 #pragma unroll
     for (int p = 0; p < Q8Cfg::PASSES; ++p) {
       const int row = p * Q8Cfg::RPP + tid / Q8Cfg::CPR, ch = tid % Q8Cfg::CPR;
       lds_store<u32x4>(lk, k8_lds_row(row) * Q8Cfg::KSTRIDE + ch * 16, k[p]);
-      if (with_v) lds_store<u32x4>(lv, row * Q8Cfg::VSTRIDE + ch * 16, v[p]);
+      if (with_v) lds_store<u32x4>(lv, (P4 ? v8_lds_row_p4(row) : row) * Q8Cfg::VSTRIDE + ch * 16, v[p]);
     }
     if (lks != nullptr && tid < Q8Cfg::BN) lks[tid] = ks;
   }
@@ -425,7 +466,8 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, float c, int nqb, int total) {
   using C = Q8Cfg;
   constexpr bool I8V = VAR == (int)QVariant::kAllInt8;
-  constexpr bool F8QK = VAR == (int)QVariant::kFp8;
+  constexpr bool P4 = VAR == (int)QVariant::kFp8P4;
+  constexpr bool F8QK = VAR == (int)QVariant::kFp8 || P4;
   __shared__ __attribute__((aligned(16))) char smem[C::KBYTES + C::VBYTES];
   __shared__ __attribute__((aligned(16))) float lks[C::BN];
   char* lk = smem;
@@ -464,7 +506,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
 
   Q8Stage st;
   st.load(Kh, Vh, KSh, 0, Nk, tid, true);
-  st.store(lk, lv, lks, tid, true);
+  st.store<P4>(lk, lv, lks, tid, true);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) st.load(Kh, Vh, KSh, (t + 1) * C::BN, Nk, tid, true);
@@ -506,6 +548,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+      const float mloc = mt;  // max over this lane's 32 keys (one MX block)
       mt = pair_max(mt) * cq;
       if (__any(mt > m_run)) {
         const float mn = fmaxf(m_run, mt);
@@ -516,7 +559,25 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
         m_run = mn;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      // P^T as 32 E4M3 bytes: byte j <-> s[j / 16][j % 16]
+      // P^T as 32 E4M3 bytes (or 32 E2M1 nibbles): element j <-> s[j / 16][j % 16]
+      // MXFP4: this lane's 32 keys share 2^e, e = floor(max log2 P) - 2, so the
+      // largest P / 2^e lies in [4, 8) (E8M0 byte e + 127 for the MFMA)
+      int e_mx = -127;
+      float inv_mx = 0.f;
+      if constexpr (P4) {
+        // the rounded product, as the running max was formed from it: the
+        // block holding the row's max then has tmax == 0 exactly (a fused
+        // multiply-add would leave the product's rounding residual, and a
+        // residual just below 0 would take e one binade too low); contraction
+        // is switched off so the compiler cannot fuse it back
+        float tmax;
+        {
+#pragma clang fp contract(off)
+          tmax = mloc * cq - m_use;
+        }
+        if (tmax != -INFINITY) e_mx = max(-127, (int)floorf(tmax) - 2);
+        inv_mx = __builtin_bit_cast(float, (uint32_t)(127 - e_mx) << 23);  // 2^-e, exact
+      }
       i32x8 pb;
 #pragma unroll
       for (int jw = 0; jw < 8; ++jw) {
@@ -526,7 +587,19 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
         const float p2 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 2], cq, -m_use));
         const float p3 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 3], cq, -m_use));
         l_run += (p0 + p1) + (p2 + p3);
-        pb[jw] = I8V ? (int)p_u8x4(p0, p1, p2, p3) : (int)e4m3x4(p0, p1, p2, p3);
+        if constexpr (P4) {
+          // nibbles 4jw .. 4jw+3: dword jw / 2, bytes 2 (jw % 2) and 2 (jw % 2) + 1
+          const uint32_t prev = (jw & 1) ? (uint32_t)pb[jw >> 1] : 0u;
+          uint32_t w = e2m1x2_into(prev, p0 * inv_mx, p1 * inv_mx, 2 * (jw & 1));
+          w = e2m1x2_into(w, p2 * inv_mx, p3 * inv_mx, 2 * (jw & 1) + 1);
+          pb[jw >> 1] = (int)w;
+        } else {
+          pb[jw] = I8V ? (int)p_u8x4(p0, p1, p2, p3) : (int)e4m3x4(p0, p1, p2, p3);
+        }
+      }
+      if constexpr (P4) {
+#pragma unroll
+        for (int k = 4; k < 8; ++k) pb[k] = 0;
       }
       // O^T += V^T P^T: lane (h, d) reads LDS rows 32h .. 32h+31 at column d
       const int r16 = lane & 15, g1 = (lane >> 4) & 1;
@@ -547,6 +620,8 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
                                                       acc, 0, 0, 0);
 #pragma unroll
           for (int j = 0; j < 16; ++j) o[mb][j] += (float)acc[j];  // |acc| < 64 * 127^2 < 2^24: exact
+        } else if constexpr (P4) {
+          o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 4, 0, 127, 0, e_mx + 127);
         } else {
           o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 0, 0, 127, 0, 127);
         }
@@ -554,7 +629,7 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
     }
     __syncthreads();
     if (t + 1 < ntiles) {
-      st.store(lk, lv, lks, tid, true);
+      st.store<P4>(lk, lv, lks, tid, true);
       __syncthreads();
     }
   }
@@ -669,6 +744,8 @@ hipError_t launch_prefill_q8(const void* q8v, const void* k8v, const void* v8v, 
   ATTN_Q8(false, 1)
   ATTN_Q8(true, 2)
   ATTN_Q8(false, 2)
+  ATTN_Q8(true, 3)
+  ATTN_Q8(false, 3)
 #undef ATTN_Q8
   return hipGetLastError();
 }
@@ -709,6 +786,12 @@ hipError_t launch_debug_qk(const void* q8, const void* k8, void* s, int Nq, int 
     hipLaunchKernelGGL(debug_qk_kernel<true>, grid, dim3(256), 0, stream, a, b, s, Nq, Nk);
   else
     hipLaunchKernelGGL(debug_qk_kernel<false>, grid, dim3(256), 0, stream, a, b, s, Nq, Nk);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_cvt_e2m1(const float* x, uint8_t* y, long n, hipStream_t stream) {
+  const long groups = n / 8;
+  hipLaunchKernelGGL(debug_cvt_e2m1_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, x, y, n);
   return hipGetLastError();
 }
 

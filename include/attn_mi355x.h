@@ -292,6 +292,21 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  float scale, int causal, void* stream);
 
 /*
+ * attn_fwd_fp8 with the probabilities in four-bit floating point: the FP4
+ * attention of the gist.science summary of "Hardware-Aware FP4
+ * FlashAttention-4" (summary and explainer).  P = exp(S - running max) is
+ * encoded as OCP E2M1 (0, 0.5, 1, 1.5, 2, 3, 4, 6; round to nearest even,
+ * clamped at 6) with one power-of-two scale 2^e per 32 consecutive keys of a
+ * query (OCP MX: e = floor(log2 max P of the block) - 2); P.V runs on the
+ * mixed fp8 x fp4 MFMA with the scales applied by the matrix cores; l sums
+ * the unquantised P.  Arguments and errors as attn_fwd_fp8.
+ */
+int attn_fwd_fp4p(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                  const float* q_scale, const float* k_scale, const float* v_scale,
+                  void* out, float* lse, int B, int H, int Nq, int Nk, int d,
+                  float scale, int causal, void* stream);
+
+/*
  * Rotation and block E4M3 quantisation of Q or K for attn_fwd_fp8 (same
  * source as attn_fwd_fp8).  x [BH, N, d] bf16, d = 128.  With signs (DEVICE,
  * d float32 values, each +1 or -1; the caller draws them once and uses the
@@ -321,10 +336,14 @@ int attn_rotate_quantize_e4m3(const void* x, const float* signs, uint8_t* x8, fl
  *   attn_fwd_fp8; d == 128.
  * attn_debug_cvt_e4m3: y[i] = E4M3(x[i]) through the same conversion
  *   routine attn_quantize_tensor_e4m3 uses (saturating); n even.
+ * attn_debug_cvt_e2m1: y[i] = E2M1 code (0 .. 15) of x[i] through the same
+ *   conversion routine attn_fwd_fp4p uses for P (clamped at 6), eight values
+ *   packed per 32-bit word as the P operand is; n a multiple of 8.
  */
 int attn_debug_qk_i32(const int8_t* q8, const int8_t* k8, int32_t* s, int Nq, int Nk, int d, void* stream);
 int attn_debug_qk_f8(const uint8_t* q8, const uint8_t* k8, float* s, int Nq, int Nk, int d, void* stream);
 int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream);
+int attn_debug_cvt_e2m1(const float* x, uint8_t* y, long n, void* stream);
 
 /* Static text for a return code. */
 const char* attn_status_str(int status);

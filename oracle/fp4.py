@@ -19,8 +19,16 @@ it).  It gives no formulas.  Readings (the plainest ones):
   * "mapping scores straight to the encoding" yields the same code as
     rounding the exact P = exp(S - m) (the code is a monotone step function
     of S - m with steps at the logarithms of the midpoints), so the oracle
-    rounds the exact P; P is taken against the final row max as in
-    oracle.quant;
+    rounds the exact P;
+  * P is the tiled recurrence's own P ([trading post], "The Flash Attention
+    algorithm" and "The online softmax recurrence"): keys are taken in
+    tiles of ``tile`` keys; for each tile the running max m is raised to
+    include it, the accumulated O and l are rescaled by exp(m_old - m_new),
+    and the tile's P = exp(S - m) is quantised before its product with V.
+    With a four-bit P the max it is taken against matters (a block's scale
+    and the rounding points move with it), so the tile width is a parameter
+    (the GPU kernel's is 64 keys); MX blocks are 32 consecutive keys from the
+    tile's start;
   * l sums the unquantised P, as in the quantised forward; Q, K are E4M3
     with per-row scales and V per-tensor E4M3, as in oracle.rotated (the
     scores are exact products of the decoded codes).
@@ -31,7 +39,9 @@ against closed forms (powers of two, the 1/16 cut-off, saturation-free
 block maxima) and against a per-element brute force over the eight codes;
 the attention against the uniform and one-dominant-key closed forms and
 against oracle.rotated's FP8 attention where every P is exact in both
-formats (tests/test_oracle_fp4.py).
+formats; the recurrence, with the quantiser replaced by the identity,
+against the plain definition for several tile widths
+(tests/test_oracle_fp4.py).
 """
 from __future__ import annotations
 
@@ -90,26 +100,40 @@ def quantize_p_mx(p, block: int = MX_BLOCK) -> np.ndarray:
     return out.reshape(Nq, nb * block)[:, :Nk]
 
 
-def attention_fp4p_head(q8, sq, k8, sk, v8, sv, scale: float, causal: bool = False):
+def attention_fp4p_head(q8, sq, k8, sk, v8, sv, scale: float, causal: bool = False, tile: int = 64,
+                        quantize=quantize_p_mx):
     """One head: scores from E4M3 codes (exact products) * sq[i] * sk[j] *
-    scale, mask, P = exp(S - m), l = sum P, O = MXFP4(P) . (decode(v8) sv) / l.
-    Returns (O, LSE) fp64."""
+    scale, masked; then the tiled recurrence, each tile's P quantised by
+    ``quantize`` (MXFP4) before its product with decode(v8) * sv; l sums the
+    unquantised P.  Returns (O, LSE) fp64."""
     Nq, Nk = q8.shape[0], k8.shape[0]
     if causal and Nq > Nk:
         raise ValueError("causal attention needs Nq <= Nk")
+    if tile < 1:
+        raise ValueError("tile must be positive")
     s = Q.e4m3_decode(q8) @ Q.e4m3_decode(k8).T
     s = s * np.asarray(sq, np.float64)[:, None] * np.asarray(sk, np.float64)[None, :] * float(scale)
     if causal:
         i = np.arange(Nq)[:, None]
         j = np.arange(Nk)[None, :]
         s = np.where(j <= i + (Nk - Nq), s, -np.inf)
-    m = s.max(axis=1)
-    p = np.exp(s - m[:, None])
-    l = p.sum(axis=1)
-    return (quantize_p_mx(p) @ (Q.e4m3_decode(v8) * float(sv))) / l[:, None], m + np.log(l)
+    vd = Q.e4m3_decode(v8) * float(sv)
+    m = np.full(Nq, -np.inf)
+    l = np.zeros(Nq)
+    acc = np.zeros((Nq, vd.shape[1]))
+    for t0 in range(0, Nk, tile):
+        st = s[:, t0:t0 + tile]
+        m_new = np.maximum(m, st.max(axis=1))
+        alpha = np.where(m == -np.inf, 0.0, np.exp(m - np.where(m_new == -np.inf, 0.0, m_new)))
+        p = np.where(st == -np.inf, 0.0, np.exp(st - np.where(m_new == -np.inf, 0.0, m_new)[:, None]))
+        l = l * alpha + p.sum(axis=1)
+        acc = acc * alpha[:, None] + quantize(p) @ vd[t0:t0 + tile]
+        m = m_new
+    return acc / l[:, None], m + np.log(l)
 
 
-def attention_fp4p(q32, k32, v32, signs, scale: float, causal: bool = False, block_rows: int = 64):
+def attention_fp4p(q32, k32, v32, signs, scale: float, causal: bool = False, block_rows: int = 64,
+                   tile: int = 64):
     """The whole forward on [..., N, d] tensors: Q and K rotated (signs, or
     None) and block-quantised to E4M3 as oracle.rotated, V per-tensor E4M3,
     P in MXFP4.  Returns (O, LSE, quantised inputs)."""
@@ -120,7 +144,7 @@ def attention_fp4p(q32, k32, v32, signs, scale: float, causal: bool = False, blo
     q8, sq, k8, sk, v8 = (shp(qi[x]) for x in ("q8", "sq", "k8", "sk", "v8"))
     outs, lses = [], []
     for i in range(n):
-        o, l = attention_fp4p_head(q8[i], sq[i], k8[i], sk[i], v8[i], qi["sv"], scale, causal)
+        o, l = attention_fp4p_head(q8[i], sq[i], k8[i], sk[i], v8[i], qi["sv"], scale, causal, tile)
         outs.append(o)
         lses.append(l)
     O = np.stack(outs).reshape(lead + outs[0].shape)

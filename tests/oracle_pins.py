@@ -874,3 +874,28 @@ def pin_fp4p_attention(attention_fp4p_head, attention_fp8_head):
     b = attention_fp8_head(Qm.e4m3_encode(qi), np.ones(2, np.float32), Qm.e4m3_encode(ki), ones_k, vc, sv,
                            float(np.log(2.0)))
     assert np.allclose(a[0], b[0], atol=1e-13, rtol=0) and np.allclose(a[1], b[1], atol=1e-13)
+
+
+def pin_fp4p_recurrence(attention_fp4p_head):
+    """With the quantiser replaced by the identity the tiled recurrence is
+    exact attention: equal to the pinned definition on the decoded inputs
+    for tile widths 1, 7, 64 and the whole row, causal or not (a row that
+    sees keys only in later tiles included)."""
+    from oracle import attention as Am
+    from oracle import quant as Qm
+    rng = np.random.default_rng(77)
+    Nq, Nk, d = 9, 150, 32
+    qc = Qm.e4m3_encode(rng.standard_normal((Nq, d)) * 60)
+    kc = Qm.e4m3_encode(rng.standard_normal((Nk, d)) * 60)
+    vc = Qm.e4m3_encode(rng.standard_normal((Nk, d)) * 60)
+    sq = rng.uniform(0.01, 0.02, Nq).astype(np.float32)
+    sk = rng.uniform(0.01, 0.02, Nk).astype(np.float32)
+    sv = np.float32(0.03)
+    qd = Qm.e4m3_decode(qc) * sq[:, None].astype(np.float64)
+    kd = Qm.e4m3_decode(kc) * sk[:, None].astype(np.float64)
+    vd = Qm.e4m3_decode(vc) * float(sv)
+    for causal in (False, True):
+        O, L = Am.attention_head(qd, kd, vd, 0.4, causal)
+        for tile in (1, 7, 64, Nk):
+            o, l = attention_fp4p_head(qc, sq, kc, sk, vc, sv, 0.4, causal, tile, lambda p: p)
+            assert np.allclose(o, O, atol=1e-12, rtol=0) and np.allclose(l, L, atol=1e-12, rtol=0)

@@ -130,6 +130,17 @@ def test_quant_entry_points_reject():
     assert f8(q=MIS) == Bd.ATTN_E_INVALID
     assert f8(Nq=9, causal=1) == Bd.ATTN_E_INVALID
     assert f8(scale=float("nan")) == Bd.ATTN_E_INVALID
+    f4 = lambda **kw: L.attn_fwd_fp4p(kw.get("q", A), A, A, A, kw.get("ks", A), kw.get("vs", A), A, A,
+                                      1, 1, kw.get("Nq", 8), 8, kw.get("d", 128), kw.get("scale", 0.1),
+                                      kw.get("causal", 0), None)
+    assert f4(d=64) == Bd.ATTN_E_UNSUPPORTED
+    assert f4(ks=None) == Bd.ATTN_E_INVALID
+    assert f4(vs=A + 2) == Bd.ATTN_E_INVALID
+    assert f4(q=MIS) == Bd.ATTN_E_INVALID
+    assert f4(Nq=9, causal=1) == Bd.ATTN_E_INVALID
+    assert f4(scale=0.0) == Bd.ATTN_E_INVALID
+    assert L.attn_debug_cvt_e2m1(A, A, 3, None) == Bd.ATTN_E_INVALID
+    assert L.attn_debug_cvt_e2m1(A + 2, A, 4, None) == Bd.ATTN_E_INVALID
     rq = lambda **kw: L.attn_rotate_quantize_e4m3(kw.get("x", A), kw.get("signs", A), A, kw.get("sc", A),
                                                   kw.get("BH", 2), kw.get("N", 64), kw.get("d", 128),
                                                   kw.get("blk", 64), None)

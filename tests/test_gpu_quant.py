@@ -432,3 +432,87 @@ def test_fp8_full_size_sampled(F):
                 assert abs(l_all[b, h, r] - L[0]) <= LSE_TOL
         print(f"  sampled max|dO|={worst:.3e}", flush=True)
         assert worst <= QO_TOL
+
+
+# ---- FP8 attention with P in MXFP4 ---------------------------------------------
+
+from oracle import fp4 as F4  # noqa: E402
+
+
+def test_e2m1_conversion_bit_exact(F):
+    """The library's fp32 -> E2M1 conversion (the one that encodes P) equals
+    the oracle's round-to-nearest-even encoding on every code value, every
+    midpoint (ties to the even code) and their fp32 neighbours, a dense
+    sweep of [0, 8) and values past the largest code; P is never negative,
+    so only non-negative inputs are part of the contract."""
+    import torch
+    grid = F4.e2m1_decode(np.arange(8)).astype(np.float32)
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
+    x = np.concatenate([grid, mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0)),
+                        np.linspace(0, 8, 4097, dtype=np.float32), np.array([6.5, 7.999, 8, 100, 1e30], np.float32),
+                        np.float32(2.0) ** -np.arange(1, 30, dtype=np.float32)]).astype(np.float32)
+    x = np.concatenate([x, np.zeros((-x.size) % 8, np.float32)])
+    print(f"  gpu: debug_cvt_e2m1 n={x.size}", flush=True)
+    y = F.debug_cvt_e2m1(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    ref = F4.e2m1_encode(x)
+    bad = np.nonzero(y.cpu().numpy() != ref)[0]
+    assert bad.size == 0, (x[bad[:8]], y.cpu().numpy()[bad[:8]], ref[bad[:8]])
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 2, 300, 300), False), ((2, 1, 77, 333), True),
+                                          ((1, 1, 128, 64), False), ((1, 2, 200, 1000), False),
+                                          ((1, 1, 260, 260), True), ((1, 1, 1, 1), False), ((1, 1, 40, 97), False)],
+                         ids=lambda x: str(x))
+def test_fp4p_small(F, shape, causal):
+    import torch
+    from tests.gpu_util import errors, from_dev
+    B, H, Nq, Nk = shape
+    w = G.Workload("fp4p_small", 93, B, H, Nq, Nk, 128, "bf16", 1.0, causal, 128 ** -0.5)
+    q, k, v = G.draw_qkv(w)
+    s_np, s_dev = _signs_dev()
+    f32 = lambda x: G.to_f32(x, "bf16")
+    O, L, qi = F4.attention_fp4p(f32(q), f32(k), f32(v), s_np, w.scale, causal, 64, tile=64)
+    q8, sq, k8, sk, v8, sv = _fp8_case(F, q, k, v, s_np, s_dev)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    print(f"  gpu: attn_fwd_fp4p {shape} causal={causal}", flush=True)
+    out, lse = F.attn_fwd_fp4p(q8, k8, v8, sq, sk, sv, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    eo, ro = errors(from_dev(out), O)
+    el, _ = errors(from_dev(lse), L)
+    print(f"  max|dO|={eo:.3e} (rel {ro:.3e}) max|dLSE|={el:.3e}", flush=True)
+    assert eo <= QO_TOL and el <= LSE_TOL
+
+
+def test_fp4p_full_size_sampled(F):
+    """B=2 H=32 N=8192 d=128 with P in MXFP4: sampled rows of sampled heads
+    against the oracle, both masks; the error against the exact definition
+    is reported next to the FP8 path's."""
+    import torch
+    from tests.gpu_util import from_dev
+    w = G.WORKLOADS["quant_8k"]
+    q, k, v = G.draw_qkv(w, threads=16)
+    f32 = lambda x: G.to_f32(x, "bf16")
+    s_np, s_dev = _signs_dev()
+    qi = RT.quantize_inputs(f32(q), f32(k), f32(v), s_np, 64)
+    q8, sq, k8, sk, v8, sv = _fp8_case(F, q, k, v, s_np, s_dev)
+    _check_quantisation(qi, q8, sq, k8, sk, v8, sv)
+    for causal in (False, True):
+        print(f"  gpu: attn_fwd_fp4p full size causal={causal}", flush=True)
+        out, lse = F.attn_fwd_fp4p(q8, k8, v8, sq, sk, sv, causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        o_all, l_all = from_dev(out), from_dev(lse)
+        assert np.isfinite(o_all).all() and np.isfinite(l_all).all()
+        rng = np.random.default_rng(6)
+        worst = 0.0
+        for bh in rng.choice(w.B * w.H, 3, replace=False):
+            b, h = divmod(int(bh), w.H)
+            rows = np.unique(np.concatenate([[0, 8191], rng.integers(0, w.Nq, 24)]))
+            for r in rows:
+                nk = r + 1 if causal else w.Nk
+                O, L = F4.attention_fp4p_head(qi["q8"][b, h][r:r + 1], qi["sq"][b, h][r:r + 1], qi["k8"][b, h][:nk],
+                                              qi["sk"][b, h][:nk], qi["v8"][b, h][:nk], qi["sv"], w.scale)
+                worst = max(worst, np.abs(o_all[b, h, r] - O[0]).max())
+                assert abs(l_all[b, h, r] - L[0]) <= LSE_TOL
+        print(f"  sampled max|dO|={worst:.3e}", flush=True)
+        assert worst <= QO_TOL

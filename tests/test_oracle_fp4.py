@@ -21,6 +21,33 @@ def test_fp4p_attention_pin():
     P.pin_fp4p_attention(F4.attention_fp4p_head, RT.attention_fp8_head)
 
 
+def test_fp4p_recurrence_pin():
+    P.pin_fp4p_recurrence(F4.attention_fp4p_head)
+
+
+def test_recurrence_without_rescale_is_caught():
+    """A recurrence that forgets to rescale the accumulated O and l when the
+    running max rises fails the recurrence pin."""
+    def no_rescale(q8, sq, k8, sk, v8, sv, scale, causal=False, tile=64, quantize=None):
+        s = Q.e4m3_decode(q8) @ Q.e4m3_decode(k8).T * sq[:, None] * sk[None, :] * scale
+        if causal:
+            Nq, Nk = s.shape
+            s = np.where(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + Nk - Nq, s, -np.inf)
+        vd = Q.e4m3_decode(v8) * float(sv)
+        m = np.full(s.shape[0], -np.inf)
+        l = np.zeros(s.shape[0])
+        acc = np.zeros((s.shape[0], vd.shape[1]))
+        for t0 in range(0, s.shape[1], tile):
+            st = s[:, t0:t0 + tile]
+            m = np.maximum(m, st.max(axis=1))
+            p = np.exp(st - m[:, None])
+            l = l + p.sum(axis=1)
+            acc = acc + quantize(p) @ vd[t0:t0 + tile]
+        return acc / l[:, None], m + np.log(l)
+    with pytest.raises(AssertionError):
+        P.pin_fp4p_recurrence(no_rescale)
+
+
 def test_whole_forward_runs_per_head():
     rng = np.random.default_rng(3)
     q, k, v = (rng.standard_normal((2, 40, 128)).astype(np.float32) for _ in range(3))
@@ -85,6 +112,7 @@ def test_mx_mistake_is_caught(mistake):
 
 
 def attn_variant(q8, sq, k8, sk, v8, sv, scale, causal=False, mistake=None):
+    # one tile (the whole row) is enough for the closed-form pins
     s = Q.e4m3_decode(q8) @ Q.e4m3_decode(k8).T
     s = s * np.asarray(sq, np.float64)[:, None] * np.asarray(sk, np.float64)[None, :] * float(scale)
     m = s.max(axis=1)
@@ -93,6 +121,15 @@ def attn_variant(q8, sq, k8, sk, v8, sv, scale, causal=False, mistake=None):
     l = pq.sum(axis=1) if mistake == "l_of_quantised_p" else p.sum(axis=1)
     vd = Q.e4m3_decode(v8) * (1.0 if mistake == "no_v_scale" else float(sv))
     return (pq @ vd) / l[:, None], m + np.log(l)
+
+
+def test_unmutated_attn_copy_equals_oracle_on_one_tile():
+    rng = np.random.default_rng(8)
+    q8, k8, v8 = (Q.e4m3_encode(rng.standard_normal((n, 16)) * 30) for n in (5, 40, 40))
+    sq, sk = np.full(5, 0.05, np.float32), np.full(40, 0.04, np.float32)
+    a = attn_variant(q8, sq, k8, sk, v8, np.float32(0.1), 0.3)
+    b = F4.attention_fp4p_head(q8, sq, k8, sk, v8, np.float32(0.1), 0.3, False, 40)
+    assert np.allclose(a[0], b[0], atol=1e-14, rtol=0) and np.allclose(a[1], b[1], atol=1e-14)
 
 
 @pytest.mark.parametrize("mistake", ["l_of_quantised_p", "no_v_scale"])
