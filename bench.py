@@ -23,8 +23,10 @@ Printed as ONE JSON line, which also carries
     with P in MXFP4), each timed the same way (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                       [--copy-calibration]
+                       [--copy-calibration] [--decode-only]
        python bench.py --traffic-from FETCH_DIR WRITE_DIR
+       python bench.py --mfma-from DIR
+       python bench.py --decode-traffic-from FETCH_DIR WRITE_DIR
 
 HBM traffic: two rocprofv3 counter runs of
     python bench.py --no-cpu-baseline --no-extra --steps 3 --warmup 1 --copy-calibration
@@ -33,6 +35,14 @@ one with --pmc FETCH_SIZE and one with --pmc WRITE_SIZE (CSV output).  The
 copies of COPY_BYTES bytes (torch's copy kernel reads and writes exactly that
 many bytes), so each counter is scaled by known bytes / what it reads for
 the copy.  --traffic-from turns the two runs into profiles/prefill_4k_traffic.json.
+
+MFMA utilisation: one rocprofv3 run of the same command with --pmc MfmaUtil
+SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE; --mfma-from turns it into
+profiles/prefill_4k_mfma.json.  Decode HBM bytes: the two traffic runs of
+    python bench.py --decode-only --steps 3 --warmup 1 --copy-calibration
+and --decode-traffic-from, giving profiles/decode_8k_traffic.json.  Each
+record carries a hash of the kernel source it was taken on and is ignored
+once that source changes.
 """
 from __future__ import annotations
 
@@ -53,16 +63,22 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4k_traffic.json")
 COPY_BYTES = 1 << 30          # bytes read (and written) by one calibration copy
 PREFILL_KERNEL = "prefill_kernel<128, true, false>"   # bf16, non-causal
+MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_4k_mfma.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8k_traffic.json")
+DECODE_KERNELS = ("decode_partial_kernel<128, true, 1>", "decode_merge_kernel")
 KERNEL_SOURCES = ["flashattention_forward_amd/csrc/prefill.hip", "flashattention_forward_amd/csrc/common.h",
-                  "flashattention_forward_amd/csrc/internal.h"]
+                  "flashattention_forward_amd/csrc/seq_shape.h"]
+DECODE_SOURCES = ["flashattention_forward_amd/csrc/decode.hip", "flashattention_forward_amd/csrc/common.h",
+                  "flashattention_forward_amd/csrc/seq_shape.h"]
 
 
-def kernel_source_sha() -> str:
-    """Hash of the prefill kernel's code with comments and blank space removed,
-    so that the counter record goes stale when the code changes, not its prose."""
+def kernel_source_sha(sources=None) -> str:
+    """Hash of a kernel's code (the prefill's by default) with comments and
+    blank space removed, so that a counter record goes stale when the code
+    changes, not its prose."""
     import re
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, p)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -71,20 +87,25 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def _current_record(path, sources=None):
+    """A committed counter record, or None if missing or taken on other code."""
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    return rec if rec.get("kernel_source_sha") == kernel_source_sha(sources) else None
+
+
 def traffic_per_launch():
     """HBM bytes per launch of the non-causal prefill kernel from the committed
     counter runs, or None if they were taken on another kernel source."""
-    try:
-        rec = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    rec = _current_record(TRAFFIC_FILE)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
-def _counter_rows(run_dir: str, counter: str):
-    """(kernel name, value) per dispatch of `counter` from a rocprofv3 CSV run."""
+def _counter_rows(run_dir: str, counter: str, with_time: bool = False):
+    """(kernel name, value[, duration ns]) per dispatch of `counter` from a
+    rocprofv3 CSV run."""
     import csv
     import glob
     rows = []
@@ -92,10 +113,39 @@ def _counter_rows(run_dir: str, counter: str):
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r.get("Counter_Name") == counter:
-                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+                    row = (r["Kernel_Name"], float(r["Counter_Value"]))
+                    if with_time:
+                        row += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),)
+                    rows.append(row)
     if not rows:
         raise SystemExit(f"no {counter} rows under {run_dir}")
     return rows
+
+
+def _write(path, rec):
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def _scaled_bytes(run_dir, counter, kernels, per_call):
+    """Counter bytes per call of the listed kernels (per_call dispatches of each
+    make one call), scaled by the copy calibration run in the same process."""
+    rows = _counter_rows(run_dir, counter)
+    copy = [v for k, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy:
+        raise SystemExit(f"{counter}: no copy-calibration dispatches under {run_dir}")
+    copy_kib = sorted(copy)[len(copy) // 2]
+    factor = COPY_BYTES / (copy_kib * 1024.0)
+    kib = 0.0
+    for name in kernels:
+        vals = [v for k, v in rows if name in k]
+        if not vals:
+            raise SystemExit(f"{counter}: no {name} dispatches under {run_dir}")
+        kib += sum(vals) / len(vals) * per_call.get(name, 1)
+    return {"counter": counter, "kib_per_call": round(kib, 1), "copy_kib_per_dispatch": round(copy_kib, 1),
+            "bytes_per_counter_byte": round(factor, 4), "bytes_per_call": round(kib * 1024.0 * factor)}
 
 
 def traffic_from(fetch_dir: str, write_dir: str) -> dict:
@@ -104,23 +154,49 @@ def traffic_from(fetch_dir: str, write_dir: str) -> dict:
     out = {"kernel": PREFILL_KERNEL, "kernel_source_sha": kernel_source_sha(), "copy_bytes": COPY_BYTES}
     total = 0.0
     for name, run_dir, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        rows = _counter_rows(run_dir, counter)
-        copy = [v for k, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
-        pre = [v for k, v in rows if PREFILL_KERNEL in k]
-        if not copy or not pre:
-            raise SystemExit(f"{counter}: need both copy and {PREFILL_KERNEL} dispatches under {run_dir}")
-        copy_kib = sorted(copy)[len(copy) // 2]
-        pre_kib = sum(pre) / len(pre)
-        factor = COPY_BYTES / (copy_kib * 1024.0)
-        out[name] = {"counter": counter, "prefill_kib_per_dispatch": round(pre_kib, 1),
-                     "copy_kib_per_dispatch": round(copy_kib, 1), "bytes_per_counter_byte": round(factor, 4),
-                     "prefill_bytes_per_launch": round(pre_kib * 1024.0 * factor)}
-        total += pre_kib * 1024.0 * factor
+        r = _scaled_bytes(run_dir, counter, [PREFILL_KERNEL], {})
+        out[name] = {"counter": counter, "prefill_kib_per_dispatch": r["kib_per_call"],
+                     "copy_kib_per_dispatch": r["copy_kib_per_dispatch"],
+                     "bytes_per_counter_byte": r["bytes_per_counter_byte"], "prefill_bytes_per_launch": r["bytes_per_call"]}
+        total += r["bytes_per_call"]
     out["hbm_bytes_per_launch"] = round(total)
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    return out
+    return _write(TRAFFIC_FILE, out)
+
+
+def mfma_from(run_dir: str) -> dict:
+    """MFMA utilisation of the non-causal prefill kernel from one rocprofv3 run
+    with --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE: rocprof's
+    derived MfmaUtil (busy cycles summed over all SIMDs / (active cycles x
+    SIMDs)), the busy cycles per SIMD, and the clock the active-cycle count
+    implies over the dispatch (GRBM_GUI_ACTIVE summed over the 8 XCDs)."""
+    util = [v for k, v in _counter_rows(run_dir, "MfmaUtil") if PREFILL_KERNEL in k]
+    busy = [v for k, v in _counter_rows(run_dir, "SQ_VALU_MFMA_BUSY_CYCLES") if PREFILL_KERNEL in k]
+    gui = [(v, t) for k, v, t in _counter_rows(run_dir, "GRBM_GUI_ACTIVE", True) if PREFILL_KERNEL in k]
+    if not util or not busy or not gui:
+        raise SystemExit(f"no {PREFILL_KERNEL} dispatches under {run_dir}")
+    n = min(len(util), len(busy), len(gui))
+    clocks = [g / 8.0 / t for g, t in gui[:n]]
+    mfmas = 1099511627776.0 / (32 * 32 * 16 * 2)          # 32x32x16 MFMAs per launch
+    rec = {"kernel": PREFILL_KERNEL, "kernel_source_sha": kernel_source_sha(), "dispatches": n,
+           "mfma_util_pct": [round(u, 2) for u in util[:n]],
+           "mfma_busy_cycles_per_simd": [round(b / 1024.0) for b in busy[:n]],
+           "busy_cycles_per_mfma": round(busy[0] / (mfmas), 2),
+           "clock_ghz": [round(c, 3) for c in clocks],
+           "dispatch_us": [round(t / 1e3, 1) for _, t in gui[:n]]}
+    return _write(MFMA_FILE, rec)
+
+
+def decode_traffic_from(fetch_dir: str, write_dir: str) -> dict:
+    """HBM bytes of one split-KV decode call (partial + merge kernels) of the
+    decode_8k workload from two counter runs of bench.py --decode-only."""
+    out = {"kernels": list(DECODE_KERNELS), "kernel_source_sha": kernel_source_sha(DECODE_SOURCES),
+           "copy_bytes": COPY_BYTES, "algorithmic_bytes": 2 * 64 * 32 * 8192 * 128 * 2}
+    total = 0
+    for name, run_dir, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        out[name] = _scaled_bytes(run_dir, counter, DECODE_KERNELS, {})
+        total += out[name]["bytes_per_call"]
+    out["hbm_bytes_per_call"] = total
+    return _write(DECODE_TRAFFIC_FILE, out)
 
 
 def copy_calibration():
@@ -198,9 +274,18 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--mfma-from", metavar="DIR")
+    ap.add_argument("--decode-traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--decode-only", action="store_true")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from(*args.traffic_from)))
+        return
+    if args.mfma_from:
+        print(json.dumps(mfma_from(args.mfma_from)))
+        return
+    if args.decode_traffic_from:
+        print(json.dumps(decode_traffic_from(*args.decode_traffic_from)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (the forward pass shards by "
@@ -217,6 +302,17 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+    if args.decode_only:
+        # the split-KV decode of decode_8k alone (for its counter runs)
+        wd = G.WORKLOADS["decode_8k"]
+        tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(wd, threads=16))
+        o = torch.empty_like(tq)
+        l = torch.empty((wd.B, wd.H, 1), device="cuda")
+        ws = torch.empty(F.workspace_bytes(wd.B, wd.H, 1, wd.Nk, wd.d, 0), device="cuda", dtype=torch.uint8)
+        _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, scale=wd.scale, out=o, lse=l, workspace=ws)],
+                                args.steps, args.warmup)
+        print(json.dumps({"workload": "decode_8k", "ms": round(per[0] * 1e3, 4)}))
+        return
     w = G.WORKLOADS["prefill_4k"]
     q, k, v = (G.to_torch(x, "bf16") for x in G.draw_qkv(w, threads=16))
     out_nc, out_c = torch.empty_like(q), torch.empty_like(q)
@@ -230,6 +326,7 @@ def main():
     value = (flops_nc + flops_c) * args.steps / total / 1e12
     achieved = flops_nc / per[0] / 1e12
     traffic = traffic_per_launch()
+    mf = _current_record(MFMA_FILE)
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -249,7 +346,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "prefill_kernel<128, bf16, non-causal>",
-                     "flops_per_launch": flops_nc},
+                     "flops_per_launch": flops_nc,
+                     "mfma_util_counted": None if mf is None else {
+                         "pct": mf["mfma_util_pct"], "clock_ghz": mf["clock_ghz"],
+                         "source": "profiles/prefill_4k_mfma.json (rocprofv3 MfmaUtil)"}},
         "kernels": {
             "prefill_noncausal": {"ms": round(per[0] * 1e3, 4), "tflops": round(flops_nc / per[0] / 1e12, 3),
                                   "frac_peak": round(flops_nc / per[0] / 1e12 / PEAK_BF16_TFLOPS, 4)},
@@ -375,6 +475,12 @@ def main():
                               "gbs_kv": round(kv_bytes / per[0] / 1e9, 1),
                               "frac_hbm_peak": round(kv_bytes / per[0] / 1e9 / PEAK_HBM_GBS, 4),
                               "kv_bytes": kv_bytes}
+        drec = _current_record(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
+        if drec is not None:
+            # all HBM bytes of the call as the counters saw them (K, V, Q, partials)
+            hb = drec["hbm_bytes_per_call"]
+            other["decode_8k"].update({"hbm_bytes_counted": hb, "gbs_counted": round(hb / per[0] / 1e9, 1),
+                                       "frac_hbm_peak_counted": round(hb / per[0] / 1e9 / PEAK_HBM_GBS, 4)})
         del tq, tk, tv, o, l, ws
         torch.cuda.empty_cache()
         # quantised forward (timing covers attn_fwd_q8 only; quantisation reported apart)

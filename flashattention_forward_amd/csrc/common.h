@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "internal.h"
+#include "seq_shape.h"
 
 namespace attn {
 

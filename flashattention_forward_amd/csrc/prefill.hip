@@ -105,7 +105,8 @@ __device__ __forceinline__ void tile_load_lds(const __amdgpu_buffer_rsrc_t& r, c
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, SeqShape sh, float c, int nqb, int total, int paired) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, SeqShape sh, float c, int nqb, int total, int paired,
+    int persist) {
   using C = PrefillCfg<D>;
   using M = Mfma<BF16>;
   typedef typename M::op8 op8;
@@ -128,283 +129,288 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   // sequences differ in length, instead take block rank j slowest over all
   // (sequence, head) pairs in plain dispatch order: the longest blocks of every
   // sequence start first and spread over all XCDs.
-  const bool packed = sh.cu_q != nullptr;
-  const int logical = packed ? (int)blockIdx.x : xcd_remap(blockIdx.x, total);
-  const int per_head = paired ? (nqb + 1) / 2 : nqb;
-  int bh, j_item;
-  if (packed) {
-    const int nh = total / per_head;
-    j_item = logical / nh;
-    bh = logical - j_item * nh;
-  } else {
-    bh = logical / per_head;
-    j_item = logical - bh * per_head;
-  }
-  const int nitems = (paired && nqb - 1 - j_item != j_item) ? 2 : 1;
-  // this (sequence, head)'s rows; Nq and Nk are its own lengths from here on
-  const SeqSpan sp = seq_span(sh, bh / sh.H, bh % sh.H);
-  const int Nq = sp.nq, Nk = sp.nk;
-  const int off = Nk - Nq;        // bottom-right causal alignment
+  // persist > 0: a grid of one workgroup per CU walks virtual blocks
+  // blockIdx.x, blockIdx.x + gridDim.x, ... (gridDim.x a multiple of 8, so each
+  // virtual block stays on its workgroup's XCD); otherwise one block each
+  for (int vb = blockIdx.x; vb < total; vb += persist ? (int)gridDim.x : total) {
+    const bool packed = sh.cu_q != nullptr;
+    const int logical = packed ? vb : xcd_remap(vb, total);
+    const int per_head = paired ? (nqb + 1) / 2 : nqb;
+    int bh, j_item;
+    if (packed) {
+      const int nh = total / per_head;
+      j_item = logical / nh;
+      bh = logical - j_item * nh;
+    } else {
+      bh = logical / per_head;
+      j_item = logical - bh * per_head;
+    }
+    const int nitems = (paired && nqb - 1 - j_item != j_item) ? 2 : 1;
+    // this (sequence, head)'s rows; Nq and Nk are its own lengths from here on
+    const SeqSpan sp = seq_span(sh, bh / sh.H, bh % sh.H);
+    const int Nq = sp.nq, Nk = sp.nk;
+    const int off = Nk - Nq;        // bottom-right causal alignment
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int grp = w >> 2, wg = w & 3;
-  const int h = lane >> 5, l32 = lane & 31;
-  const size_t qbase = sp.q_row0 * D;
-  const size_t kbase = sp.k_row0 * D;
-  const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
-  const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
-  const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int grp = w >> 2, wg = w & 3;
+    const int h = lane >> 5, l32 = lane & 31;
+    const size_t qbase = sp.q_row0 * D;
+    const size_t kbase = sp.k_row0 * D;
+    const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
+    const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
+    const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
 
-  // direct global -> LDS loads of one tile, issued by the 4 waves of group 0
-  // only: wave wg fills 1 KB blocks LPG*wg .. LPG*wg + LPG-1; lane i lands at
-  // byte 16 i of its block (row i/SPR, slot i%SPR) and therefore fetches
-  // global chunk slot ^ swizzle(row).  Keys past Nk read as 0 (buffer range check).
-  uint32_t gk_off[C::LPG], gv_off[C::LPG];
-#pragma unroll
-  for (int i = 0; i < C::LPG; ++i) {
-    const int blk = C::LPG * wg + i;
-    const int row = blk * C::RPI + lane / C::SPR, slot = lane % C::SPR;
-    gk_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ k_swz<D>(row));
-    gv_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ v_swz<D>(row));
-  }
-  // load q of the NLD a wave issues per G phase: K(tk) blocks first, then V(tv)
-  typedef __amdgpu_buffer_rsrc_t Rsrc;
-  auto issue_load = [&](const Rsrc& rk_, const Rsrc& rv_, int q, char* ldk, char* ldv, int tk, int tv) {
-    if (q < C::LPG)
-      tile_load_lds(rk_, ldk + 1024 * (C::LPG * wg + q), (uint32_t)tk * C::TILEB + gk_off[q]);
-    else
-      tile_load_lds(rv_, ldv + 1024 * (C::LPG * wg + q - C::LPG), (uint32_t)tv * C::TILEB + gv_off[q - C::LPG]);
-  };
-  // per-lane LDS operand offsets (constant across tiles)
-  uint32_t ka_off[C::KSTEPS];  // K operand, row l32 (+32 per key block), logical slot 2kk+h
-#pragma unroll
-  for (int kk = 0; kk < C::KSTEPS; ++kk) ka_off[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ k_swz<D>(l32));
-  const int r16 = lane & 15, g1 = (lane >> 4) & 1;
-  const int vrow = (r16 >> 2) + 4 * h;  // + 16 per key group, + 8 for the second read
-  uint32_t va_off[C::MB_O];            // V^T operand: columns 32mb + 16g1 + 4(r16&3)
-#pragma unroll
-  for (int mb = 0; mb < C::MB_O; ++mb) {
-    const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
-    va_off[mb] = vrow * C::ROWB + 16 * ((col >> 3) ^ v_swz<D>(vrow)) + 2 * (col & 7);
-  }
-  auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i%NB, k-step i/NB
-    return lds_load<op8>(lk, ka_off[i / C::NB] + (i % C::NB) * 32 * C::ROWB);
-  };
-  auto va_load = [&](const char* lv, int j) {  // V^T operand of O^T step j: 16-key group j/MB_O, d block j%MB_O
-    const uint32_t a0 = va_off[j % C::MB_O] + 16 * (j / C::MB_O) * C::ROWB;
-    const s16x4 lo = lds_read_tr16(lv, a0);
-    const s16x4 hi = lds_read_tr16(lv, a0 + 8 * C::ROWB);
-    return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+    // direct global -> LDS loads of one tile, issued by the 4 waves of group 0
+    // only: wave wg fills 1 KB blocks LPG*wg .. LPG*wg + LPG-1; lane i lands at
+    // byte 16 i of its block (row i/SPR, slot i%SPR) and therefore fetches
+    // global chunk slot ^ swizzle(row).  Keys past Nk read as 0 (buffer range check).
+    uint32_t gk_off[C::LPG], gv_off[C::LPG];
+  #pragma unroll
+    for (int i = 0; i < C::LPG; ++i) {
+      const int blk = C::LPG * wg + i;
+      const int row = blk * C::RPI + lane / C::SPR, slot = lane % C::SPR;
+      gk_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ k_swz<D>(row));
+      gv_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ v_swz<D>(row));
+    }
+    // load q of the NLD a wave issues per G phase: K(tk) blocks first, then V(tv)
+    typedef __amdgpu_buffer_rsrc_t Rsrc;
+    auto issue_load = [&](const Rsrc& rk_, const Rsrc& rv_, int q, char* ldk, char* ldv, int tk, int tv) {
+      if (q < C::LPG)
+        tile_load_lds(rk_, ldk + 1024 * (C::LPG * wg + q), (uint32_t)tk * C::TILEB + gk_off[q]);
+      else
+        tile_load_lds(rv_, ldv + 1024 * (C::LPG * wg + q - C::LPG), (uint32_t)tv * C::TILEB + gv_off[q - C::LPG]);
+    };
+    // per-lane LDS operand offsets (constant across tiles)
+    uint32_t ka_off[C::KSTEPS];  // K operand, row l32 (+32 per key block), logical slot 2kk+h
+  #pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) ka_off[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ k_swz<D>(l32));
+    const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+    const int vrow = (r16 >> 2) + 4 * h;  // + 16 per key group, + 8 for the second read
+    uint32_t va_off[C::MB_O];            // V^T operand: columns 32mb + 16g1 + 4(r16&3)
+  #pragma unroll
+    for (int mb = 0; mb < C::MB_O; ++mb) {
+      const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
+      va_off[mb] = vrow * C::ROWB + 16 * ((col >> 3) ^ v_swz<D>(vrow)) + 2 * (col & 7);
+    }
+    auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i%NB, k-step i/NB
+      return lds_load<op8>(lk, ka_off[i / C::NB] + (i % C::NB) * 32 * C::ROWB);
+    };
+    auto va_load = [&](const char* lv, int j) {  // V^T operand of O^T step j: 16-key group j/MB_O, d block j%MB_O
+      const uint32_t a0 = va_off[j % C::MB_O] + 16 * (j / C::MB_O) * C::ROWB;
+      const s16x4 lo = lds_read_tr16(lv, a0);
+      const s16x4 hi = lds_read_tr16(lv, a0 + 8 * C::ROWB);
+      return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
-  for (int item = 0; item < nitems; ++item) {
-    const int qb = paired ? (item == 0 ? nqb - 1 - j_item : j_item) : (CAUSAL ? nqb - 1 - j_item : j_item);
-    const int q0 = qb * C::BM;
-    if (q0 >= Nq) continue;  // past a short packed sequence (uniform over the workgroup)
-    // B operand of S^T = K Q^T: lane holds Q[qrow][16kk + 8h .. +7]; rows past Nq read as 0
-    const int qmin_w = q0 + 128 * grp + 32 * wg;  // smallest query row of this wave
-    const int qrow = qmin_w + l32;
-    op8 qop[C::KSTEPS];
-#pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk)
-      qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)qrow * C::ROWB + (16 * kk + 8 * h) * 2));
-    // keep the Q loads ahead of the first tile's: the in-order load counter then
-    // retires them before the first tile is read, and no wait on them lands in the loop
-    __builtin_amdgcn_sched_barrier(0);
+    for (int item = 0; item < nitems; ++item) {
+      const int qb = paired ? (item == 0 ? nqb - 1 - j_item : j_item) : (CAUSAL ? nqb - 1 - j_item : j_item);
+      const int q0 = qb * C::BM;
+      if (q0 >= Nq) continue;  // past a short packed sequence (uniform over the workgroup)
+      // B operand of S^T = K Q^T: lane holds Q[qrow][16kk + 8h .. +7]; rows past Nq read as 0
+      const int qmin_w = q0 + 128 * grp + 32 * wg;  // smallest query row of this wave
+      const int qrow = qmin_w + l32;
+      op8 qop[C::KSTEPS];
+  #pragma unroll
+      for (int kk = 0; kk < C::KSTEPS; ++kk)
+        qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)qrow * C::ROWB + (16 * kk + 8 * h) * 2));
+      // keep the Q loads ahead of the first tile's: the in-order load counter then
+      // retires them before the first tile is read, and no wait on them lands in the loop
+      __builtin_amdgcn_sched_barrier(0);
 
-    int kv_end = Nk;
-    if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
-    const int T = max(0, (kv_end + C::BN - 1) / C::BN);  // 0: no key visible to the block
+      int kv_end = Nk;
+      if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
+      const int T = max(0, (kv_end + C::BN - 1) / C::BN);  // 0: no key visible to the block
 
-    f32x16 o[C::MB_O];
-#pragma unroll
-    for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
-    f32x16 s[C::NB];  // S(t) between its GEMM and softmax phases
-    op8 pb[C::NG];    // P(t) between its softmax phase and the next GEMM phase
-    float m_run = -INFINITY, l_run = 0.f;
+      f32x16 o[C::MB_O];
+  #pragma unroll
+      for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
+      f32x16 s[C::NB];  // S(t) between its GEMM and softmax phases
+      op8 pb[C::NG];    // P(t) between its softmax phase and the next GEMM phase
+      float m_run = -INFINITY, l_run = 0.f;
 
-    // ---- G_t: S(t) (t < T) and O += P(t-1) V(t-1) (t >= 1), MFMA streams interleaved;
-    // lk holds K(t), lv holds V(t-1).  With LD (group 0) it also issues the loads
-    // of K(t+1) into ldk and V(t) into ldv, one every STEP MFMA steps, so that the
-    // address unit sees a steady trickle rather than every wave's loads at once.
-    // K(t+1) is loaded even when t+1 = T: those rows read as 0 or are never used.
-    auto gemm_phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool LD, int t, const char* lk, const char* lv,
-                          char* ldk, char* ldv) {
-      constexpr int STEP = C::NA / C::NLD;
-      const bool do_s = t < T, do_pv = t >= 1;
-      if (do_s && do_pv) {
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
-        constexpr int PF = 4;  // operand reads in flight per stream
-        op8 ka[PF], va[PF];
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-          ka[i] = ka_load(lk, i);
-          va[i] = va_load(lv, i);
-        }
-#pragma unroll
-        for (int i = 0; i < C::NA; ++i) {
-          const op8 a = ka[i % PF], b = va[i % PF];
-          if (i + PF < C::NA) {
-            ka[i % PF] = ka_load(lk, i + PF);
-            va[i % PF] = va_load(lv, i + PF);
+      // ---- G_t: S(t) (t < T) and O += P(t-1) V(t-1) (t >= 1), MFMA streams interleaved;
+      // lk holds K(t), lv holds V(t-1).  With LD (group 0) it also issues the loads
+      // of K(t+1) into ldk and V(t) into ldv, one every STEP MFMA steps, so that the
+      // address unit sees a steady trickle rather than every wave's loads at once.
+      // K(t+1) is loaded even when t+1 = T: those rows read as 0 or are never used.
+      auto gemm_phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool LD, int t, const char* lk, const char* lv,
+                            char* ldk, char* ldv) {
+        constexpr int STEP = C::NA / C::NLD;
+        const bool do_s = t < T, do_pv = t >= 1;
+        if (do_s && do_pv) {
+  #pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
+          constexpr int PF = 4;  // operand reads in flight per stream
+          op8 ka[PF], va[PF];
+  #pragma unroll
+          for (int i = 0; i < PF; ++i) {
+            ka[i] = ka_load(lk, i);
+            va[i] = va_load(lv, i);
           }
-          s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
-          o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
-          if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
-        }
-        // issue order: the first PF steps' operand reads, then per step its two
-        // MFMAs each followed by the reads of the step PF ahead, then its load
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * PF, 0);
-#pragma unroll
-        for (int i = 0; i < C::NA; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-          if (LD && i % STEP == STEP - 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-        }
-      } else if (do_s) {
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
-        op8 ka[2];
-        ka[0] = ka_load(lk, 0);
-        ka[1] = ka_load(lk, 1);
-#pragma unroll
-        for (int i = 0; i < C::NA; ++i) {
-          const op8 a = ka[i & 1];
-          if (i + 2 < C::NA) ka[i & 1] = ka_load(lk, i + 2);
-          s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
-          if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
-        }
-      } else if (do_pv) {
-        op8 va[2];
-        va[0] = va_load(lv, 0);
-        va[1] = va_load(lv, 1);
-#pragma unroll
-        for (int i = 0; i < C::NC; ++i) {
-          const op8 b = va[i & 1];
-          if (i + 2 < C::NC) va[i & 1] = va_load(lv, i + 2);
-          o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
-        }
-      }
-    };
-
-    // ---- X_t: mask, running max, rescale, P(t) = exp2(S c - m), row sum
-    auto softmax_phase = [&](int t) {
-      const int kv0 = t * C::BN;
-      if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
-        const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
+  #pragma unroll
+          for (int i = 0; i < C::NA; ++i) {
+            const op8 a = ka[i % PF], b = va[i % PF];
+            if (i + PF < C::NA) {
+              ka[i % PF] = ka_load(lk, i + PF);
+              va[i % PF] = va_load(lv, i + PF);
+            }
+            s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
+            o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
+            if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
           }
-      }
-      float mx[C::NB];
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        mx[nb] = fmaxf(s[nb][0], s[nb][1]);
-#pragma unroll
-        for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
-      }
-#pragma unroll
-      for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
-      const float mt = pair_max(mx[0]) * c;
-      float alpha = 1.f;
-      if (__any(mt > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mt);
-        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int g = 0; g < C::NG; ++g) {
-        const int nb = g >> 1, tt = g & 1;
-        op2 pr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j], c, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use));
-          pr[j] = M::pack2(p0, p1);
-          lsum[j] += p0 + p1;
+          // issue order: the first PF steps' operand reads, then per step its two
+          // MFMAs each followed by the reads of the step PF ahead, then its load
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * PF, 0);
+  #pragma unroll
+          for (int i = 0; i < C::NA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            if (LD && i % STEP == STEP - 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+          }
+        } else if (do_s) {
+  #pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
+          op8 ka[2];
+          ka[0] = ka_load(lk, 0);
+          ka[1] = ka_load(lk, 1);
+  #pragma unroll
+          for (int i = 0; i < C::NA; ++i) {
+            const op8 a = ka[i & 1];
+            if (i + 2 < C::NA) ka[i & 1] = ka_load(lk, i + 2);
+            s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
+            if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
+          }
+        } else if (do_pv) {
+          op8 va[2];
+          va[0] = va_load(lv, 0);
+          va[1] = va_load(lv, 1);
+  #pragma unroll
+          for (int i = 0; i < C::NC; ++i) {
+            const op8 b = va[i & 1];
+            if (i + 2 < C::NC) va[i & 1] = va_load(lv, i + 2);
+            o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
+          }
         }
-        pb[g] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                        __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+
+      // ---- X_t: mask, running max, rescale, P(t) = exp2(S c - m), row sum
+      auto softmax_phase = [&](int t) {
+        const int kv0 = t * C::BN;
+        if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
+          const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
+  #pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
+              if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
+            }
+        }
+        float mx[C::NB];
+  #pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          mx[nb] = fmaxf(s[nb][0], s[nb][1]);
+  #pragma unroll
+          for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
+        }
+  #pragma unroll
+        for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
+        const float mt = pair_max(mx[0]) * c;
+        float alpha = 1.f;
+        if (__any(mt > m_run + kRescaleThreshold)) {
+          const float m_new = fmaxf(m_run, mt);
+          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+  #pragma unroll
+          for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int g = 0; g < C::NG; ++g) {
+          const int nb = g >> 1, tt = g & 1;
+          op2 pr[4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j], c, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use));
+            pr[j] = M::pack2(p0, p1);
+            lsum[j] += p0 + p1;
+          }
+          pb[g] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                          __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        l_run = fmaf(l_run, alpha, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+      };
+
+      // prologue: K(0) into LDS
+      if (grp == 0) {
+  #pragma unroll
+        for (int q = 0; q < C::LPG; ++q) issue_load(rk, rv, q, k0s, nullptr, 0, 0);
       }
-      l_run = fmaf(l_run, alpha, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
-    };
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
 
-    // prologue: K(0) into LDS
-    if (grp == 0) {
-#pragma unroll
-      for (int q = 0; q < C::LPG; ++q) issue_load(rk, rv, q, k0s, nullptr, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // phase p: group 0 runs phase p of its own sequence G_0 X_0 G_1 X_1 ... G_T,
-    // group 1 runs phase p-1.  K(s+1) and V(s) are loaded by group 0 during its
-    // G_s in phase 2s (into buffers last read in phases 2s-2 and 2s-1) and
-    // waited for at the end of phase 2s+1.  K(t) lives in buffer t%2, V(t) in
-    // buffer t%2, so the buffer roles repeat every 4 phases.
-    auto phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool EVEN, int p, const char* gk, const char* gv, char* ldk,
-                     char* ldv) {
-      const int mp = p - grp;
-      if (mp >= 0 && mp <= 2 * T) {
-        if ((mp & 1) == 0) {
-          __builtin_amdgcn_s_setprio(1);
-          gemm_phase(rk_, rv_, EVEN, mp >> 1, gk, gv, ldk, ldv);
-          __builtin_amdgcn_s_setprio(0);
-        } else {
-          softmax_phase(mp >> 1);
+      // phase p: group 0 runs phase p of its own sequence G_0 X_0 G_1 X_1 ... G_T,
+      // group 1 runs phase p-1.  K(s+1) and V(s) are loaded by group 0 during its
+      // G_s in phase 2s (into buffers last read in phases 2s-2 and 2s-1) and
+      // waited for at the end of phase 2s+1.  K(t) lives in buffer t%2, V(t) in
+      // buffer t%2, so the buffer roles repeat every 4 phases.
+      auto phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool EVEN, int p, const char* gk, const char* gv, char* ldk,
+                       char* ldv) {
+        const int mp = p - grp;
+        if (mp >= 0 && mp <= 2 * T) {
+          if ((mp & 1) == 0) {
+            __builtin_amdgcn_s_setprio(1);
+            gemm_phase(rk_, rv_, EVEN, mp >> 1, gk, gv, ldk, ldv);
+            __builtin_amdgcn_s_setprio(0);
+          } else {
+            softmax_phase(mp >> 1);
+          }
+        }
+        if (!EVEN) {
+          // once per tile: the tile loads issued in phase p-1 have landed in every
+          // wave's part of LDS, and every wave is done with the buffers they replace
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+        }
+        // no barrier after even phases: nothing read in phase p+1 was written in
+        // phase p, and letting the groups drift within a tile measured faster
+        // than holding them in step
+      };
+      const int nphase = 2 * T + 2;  // even
+      for (int p = 0; p < nphase; p += 4) {
+        phase(rk, rv, true, p, k0s, v1s, k1s, v0s);  // G of even t: K(t) in k0, V(t-1) in v1; loads K(t+1)->k1, V(t)->v0
+        phase(rk, rv, false, p + 1, k0s, v1s, k1s, v0s);
+        if (p + 2 < nphase) {
+          phase(rk, rv, true, p + 2, k1s, v0s, k0s, v1s);  // G of odd t
+          phase(rk, rv, false, p + 3, k1s, v0s, k0s, v1s);
         }
       }
-      if (!EVEN) {
-        // once per tile: the tile loads issued in phase p-1 have landed in every
-        // wave's part of LDS, and every wave is done with the buffers they replace
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
-      // no barrier after even phases: nothing read in phase p+1 was written in
-      // phase p, and letting the groups drift within a tile measured faster
-      // than holding them in step
-    };
-    const int nphase = 2 * T + 2;  // even
-    for (int p = 0; p < nphase; p += 4) {
-      phase(rk, rv, true, p, k0s, v1s, k1s, v0s);  // G of even t: K(t) in k0, V(t-1) in v1; loads K(t+1)->k1, V(t)->v0
-      phase(rk, rv, false, p + 1, k0s, v1s, k1s, v0s);
-      if (p + 2 < nphase) {
-        phase(rk, rv, true, p + 2, k1s, v0s, k0s, v1s);  // G of odd t
-        phase(rk, rv, false, p + 3, k1s, v0s, k0s, v1s);
-      }
-    }
 
-    // ---- epilogue: combine the half-wave row sums, normalise, write O and LSE
-    // a row that saw no key (packed batches only) has l = 0: O = 0, LSE = -inf
-    const float l_tot = pair_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < Nq) {
-      uint16_t* dst = O + qbase + (size_t)qrow * D;
-#pragma unroll
-      for (int mb = 0; mb < C::MB_O; ++mb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const op2 x0 = M::pack2(o[mb][4 * g + 0] * inv, o[mb][4 * g + 1] * inv);
-          const op2 x1 = M::pack2(o[mb][4 * g + 2] * inv, o[mb][4 * g + 3] * inv);
-          u32x2 u;
-          u[0] = __builtin_bit_cast(uint32_t, x0);
-          u[1] = __builtin_bit_cast(uint32_t, x1);
-          *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g + 4 * h) = u;
-        }
-      if (LSE != nullptr && h == 0) LSE[sp.q_row0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
-    }
-  }  // work items
+      // ---- epilogue: combine the half-wave row sums, normalise, write O and LSE
+      // a row that saw no key (packed batches only) has l = 0: O = 0, LSE = -inf
+      const float l_tot = pair_sum(l_run);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (qrow < Nq) {
+        uint16_t* dst = O + qbase + (size_t)qrow * D;
+  #pragma unroll
+        for (int mb = 0; mb < C::MB_O; ++mb)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const op2 x0 = M::pack2(o[mb][4 * g + 0] * inv, o[mb][4 * g + 1] * inv);
+            const op2 x1 = M::pack2(o[mb][4 * g + 2] * inv, o[mb][4 * g + 3] * inv);
+            u32x2 u;
+            u[0] = __builtin_bit_cast(uint32_t, x0);
+            u[1] = __builtin_bit_cast(uint32_t, x1);
+            *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g + 4 * h) = u;
+          }
+        if (LSE != nullptr && h == 0) LSE[sp.q_row0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+      }
+    }  // work items
+  }  // virtual blocks
 }
 
 // compute units of the current device (asked on every call: no cached state)
@@ -428,10 +434,16 @@ static hipError_t launch_t(const void* q, const void* k, const void* v, void* ou
   const int paired = (CAUSAL && sh.cu_q == nullptr && pairs >= 4L * device_cu_count()) ? 1 : 0;
   const int total = (paired ? (nqb + 1) / 2 : nqb) * nseq * sh.H;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<D, BF16, CAUSAL>), dim3(total), dim3(C::NT), 0, stream,
+  // items of equal work (dense non-causal, or paired causal) run on a
+  // persistent grid of one workgroup per CU: no workgroup launch between
+  // items; packed and unpaired causal grids keep the hardware's dynamic order
+  const int cus = device_cu_count() & ~7;
+  const int persist = (sh.cu_q == nullptr && (!CAUSAL || paired) && cus >= 8 && total > cus) ? 1 : 0;
+  const int grid = persist ? cus : total;
+  hipLaunchKernelGGL((prefill_kernel<D, BF16, CAUSAL>), dim3(grid), dim3(C::NT), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, sh, scale * kLog2e, nqb,
-                     total, paired);
+                     total, paired, persist);
   return hipGetLastError();
 }
 
