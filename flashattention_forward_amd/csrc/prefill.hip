@@ -165,7 +165,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     // byte 16 i of its block (row i/SPR, slot i%SPR) and therefore fetches
     // global chunk slot ^ swizzle(row).  Keys past Nk read as 0 (buffer range check).
     uint32_t gk_off[C::LPG], gv_off[C::LPG];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < C::LPG; ++i) {
       const int blk = C::LPG * wg + i;
       const int row = blk * C::RPI + lane / C::SPR, slot = lane % C::SPR;
@@ -182,12 +182,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     };
     // per-lane LDS operand offsets (constant across tiles)
     uint32_t ka_off[C::KSTEPS];  // K operand, row l32 (+32 per key block), logical slot 2kk+h
-  #pragma unroll
+#pragma unroll
     for (int kk = 0; kk < C::KSTEPS; ++kk) ka_off[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ k_swz<D>(l32));
     const int r16 = lane & 15, g1 = (lane >> 4) & 1;
     const int vrow = (r16 >> 2) + 4 * h;  // + 16 per key group, + 8 for the second read
     uint32_t va_off[C::MB_O];            // V^T operand: columns 32mb + 16g1 + 4(r16&3)
-  #pragma unroll
+#pragma unroll
     for (int mb = 0; mb < C::MB_O; ++mb) {
       const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
       va_off[mb] = vrow * C::ROWB + 16 * ((col >> 3) ^ v_swz<D>(vrow)) + 2 * (col & 7);
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       const int qmin_w = q0 + 128 * grp + 32 * wg;  // smallest query row of this wave
       const int qrow = qmin_w + l32;
       op8 qop[C::KSTEPS];
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < C::KSTEPS; ++kk)
         qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)qrow * C::ROWB + (16 * kk + 8 * h) * 2));
       // keep the Q loads ahead of the first tile's: the in-order load counter then
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       const int T = max(0, (kv_end + C::BN - 1) / C::BN);  // 0: no key visible to the block
 
       f32x16 o[C::MB_O];
-  #pragma unroll
+#pragma unroll
       for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
       f32x16 s[C::NB];  // S(t) between its GEMM and softmax phases
       op8 pb[C::NG];    // P(t) between its softmax phase and the next GEMM phase
@@ -238,16 +238,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         constexpr int STEP = C::NA / C::NLD;
         const bool do_s = t < T, do_pv = t >= 1;
         if (do_s && do_pv) {
-  #pragma unroll
+#pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
           constexpr int PF = 4;  // operand reads in flight per stream
           op8 ka[PF], va[PF];
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < PF; ++i) {
             ka[i] = ka_load(lk, i);
             va[i] = va_load(lv, i);
           }
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < C::NA; ++i) {
             const op8 a = ka[i % PF], b = va[i % PF];
             if (i + PF < C::NA) {
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
           // issue order: the first PF steps' operand reads, then per step its two
           // MFMAs each followed by the reads of the step PF ahead, then its load
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * PF, 0);
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < C::NA; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
@@ -270,12 +270,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             if (LD && i % STEP == STEP - 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
           }
         } else if (do_s) {
-  #pragma unroll
+#pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
           op8 ka[2];
           ka[0] = ka_load(lk, 0);
           ka[1] = ka_load(lk, 1);
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < C::NA; ++i) {
             const op8 a = ka[i & 1];
             if (i + 2 < C::NA) ka[i & 1] = ka_load(lk, i + 2);
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
           op8 va[2];
           va[0] = va_load(lv, 0);
           va[1] = va_load(lv, 1);
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < C::NC; ++i) {
             const op8 b = va[i & 1];
             if (i + 2 < C::NC) va[i & 1] = va_load(lv, i + 2);
@@ -300,39 +300,39 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         const int kv0 = t * C::BN;
         if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
           const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
-  #pragma unroll
+#pragma unroll
           for (int nb = 0; nb < C::NB; ++nb)
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
               if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
             }
         }
         float mx[C::NB];
-  #pragma unroll
+#pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
           mx[nb] = fmaxf(s[nb][0], s[nb][1]);
-  #pragma unroll
+#pragma unroll
           for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
         }
-  #pragma unroll
+#pragma unroll
         for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
         const float mt = pair_max(mx[0]) * c;
         float alpha = 1.f;
         if (__any(mt > m_run + kRescaleThreshold)) {
           const float m_new = fmaxf(m_run, mt);
           alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-  #pragma unroll
+#pragma unroll
           for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
           m_run = m_new;
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < C::NG; ++g) {
           const int nb = g >> 1, tt = g & 1;
           op2 pr[4];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j], c, -m_use));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use));
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
 
       // prologue: K(0) into LDS
       if (grp == 0) {
-  #pragma unroll
+#pragma unroll
         for (int q = 0; q < C::LPG; ++q) issue_load(rk, rv, q, k0s, nullptr, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt(0);
@@ -396,9 +396,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       if (qrow < Nq) {
         uint16_t* dst = O + qbase + (size_t)qrow * D;
-  #pragma unroll
+#pragma unroll
         for (int mb = 0; mb < C::MB_O; ++mb)
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < 4; ++g) {
             const op2 x0 = M::pack2(o[mb][4 * g + 0] * inv, o[mb][4 * g + 1] * inv);
             const op2 x1 = M::pack2(o[mb][4 * g + 2] * inv, o[mb][4 * g + 3] * inv);
