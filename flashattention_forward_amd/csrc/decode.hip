@@ -19,6 +19,8 @@
 // A second kernel merges the ranges: LSE = M + ln sum_s exp(LSE_s - M),
 // O = sum_s exp(LSE_s - LSE) O_s -- the same running-statistics update
 // applied to states over disjoint key ranges.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -186,6 +188,189 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
   }
 }
 
+// ---------------------------------------------------------- grouped, on MFMA
+// With HG = 4 or 8 query heads per K/V head the vector-ALU kernel above does
+// HG dot products and HG cross-lane reductions per row and becomes bound by
+// the vector ALU, not by HBM.  This kernel moves both products to the matrix
+// cores, in the operand layouts of the prefill kernel with the HG heads as
+// its query columns: each wave streams 32-key tiles of the workgroup's key
+// range, S^T = K Q^T with the K tile as the A operand loaded from HBM straight
+// into registers and the HG queries as B columns (columns past HG read 0),
+// the online softmax on the 16 scores a lane holds for its head, then
+// O^T += V^T P^T with the V tile read transposed from wave-private LDS.  The
+// next tile's K and V loads are in flight while the current tile is used.
+// The matrix cores run 32 - HG empty columns; they have the throughput to
+// spare, and the vector ALU does about a tenth of the other kernel's work.
+__device__ __forceinline__ void dec_lds_load(const __amdgpu_buffer_rsrc_t& r, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+// V tile swizzle (16-byte slot XOR a function of the row): the transposing
+// reads of 16-lane groups (4 consecutive rows, 32 bytes each) hit distinct banks
+template <int D>
+__device__ __forceinline__ int dec_v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+constexpr float kDecRescaleThreshold = 8.0f;  // log2 units, as the prefill kernel
+
+template <int D, bool BF16, int HG>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    float* __restrict__ Opart, float* __restrict__ Lpart, int Nk, float c, int splits, int H, int group) {
+  using M = Mfma<BF16>;
+  typedef typename M::op8 op8;
+  typedef typename M::op2 op2;
+  constexpr int BN = 32, ROWB = D * 2, SPR = ROWB / 16, RPI = 1024 / ROWB;
+  constexpr int KSTEPS = D / 16, MB_O = D / 32, TILEB = BN * ROWB, LPW = TILEB / 1024;
+  static_assert(4 * HG * D * 4 <= 4 * 2 * TILEB, "the merge area fits in the V buffers");
+  __shared__ __attribute__((aligned(1024))) char vbuf[4][2][TILEB];
+  __shared__ float mst[4][HG], lst[4][HG];
+
+  const int wgi = blockIdx.x / splits, split = blockIdx.x - wgi * splits;
+  const int s0 = (int)(((long)split * Nk) / splits), s1 = (int)(((long)(split + 1) * Nk) / splits);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bh0 = wgi * HG;
+  const int b = bh0 / H, h0 = bh0 - b * H;
+  const size_t kbase = ((size_t)b * (H / group) + h0 / group) * Nk * D;
+  const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * ROWB);
+  const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * ROWB);
+  const auto rq = make_rsrc(Q + (size_t)bh0 * D, (uint32_t)HG * ROWB);
+
+  // B operand: head l32 (its row of Q), d = 16kk + 8h .. +7; columns >= HG read 0
+  op8 qop[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)l32 * ROWB + (2 * kk + h) * 16));
+
+  // V^T operand offsets in a V tile (rows = keys), as the prefill reads them
+  const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+  const int vrow = (r16 >> 2) + 4 * h;
+  uint32_t va_off[MB_O];
+#pragma unroll
+  for (int mb = 0; mb < MB_O; ++mb) {
+    const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
+    va_off[mb] = vrow * ROWB + 16 * ((col >> 3) ^ dec_v_swz<D>(vrow)) + 2 * (col & 7);
+  }
+
+  const int ntile = (s1 - s0 + BN - 1) / BN;  // wave w takes tiles w, w + 4, ...
+  f32x16 o[MB_O];
+#pragma unroll
+  for (int mb = 0; mb < MB_O; ++mb) o[mb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  op8 kr[2][KSTEPS];
+
+  // K rows key0 + l32 into registers (A operand: chunk 2kk + h), the V tile
+  // into this wave's LDS buffer; rows past Nk read 0, keys past s1 are masked
+  auto load_tile = [&](auto bc, int t) {
+    constexpr int BUF = decltype(bc)::value;
+    const int key0 = s0 + t * BN;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      kr[BUF][kk] = __builtin_bit_cast(op8, buf_load16(rk, (uint32_t)(key0 + l32) * ROWB + (2 * kk + h) * 16));
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int row = i * RPI + lane / SPR, slot = lane % SPR;
+      dec_lds_load(rv, vbuf[w][BUF] + 1024 * i, (uint32_t)(key0 + row) * ROWB + 16 * (slot ^ dec_v_swz<D>(row)));
+    }
+  };
+  // loads complete in order: with the next tile's KSTEPS + LPW loads issued
+  // after this tile's, waiting for at most that many outstanding is enough
+  constexpr int VM = KSTEPS + LPW;
+  constexpr int kWaitNext = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
+  auto step = [&](auto bc, int t) {
+    constexpr int BUF = decltype(bc)::value;
+    const bool more = t + 4 < ntile;
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS reads done before the other buffer is refilled
+      load_tile(std::integral_constant<int, BUF ^ 1>{}, t + 4);
+      __builtin_amdgcn_s_waitcnt(kWaitNext);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) s = M::mma(kr[BUF][kk], qop[kk], s);
+    const int key0 = s0 + t * BN;
+    if (key0 + BN > s1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + 8 * (i >> 2) + 4 * h + (i & 3) >= s1) s[i] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    const float mt = pair_max(mx) * c;
+    if (__any(mt > m_run + kDecRescaleThreshold)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+#pragma unroll
+      for (int mb = 0; mb < MB_O; ++mb) o[mb] *= alpha;
+      l_run *= alpha;
+      m_run = mn;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    op8 pb[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      op2 pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + 2 * j], c, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + 2 * j + 1], c, -m_use));
+        pr[j] = M::pack2(p0, p1);
+        l_run += p0 + p1;
+      }
+      pb[tt] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const char* lv = vbuf[w][BUF];
+#pragma unroll
+    for (int j = 0; j < 2 * MB_O; ++j) {
+      const uint32_t a0 = va_off[j % MB_O] + 16 * (j / MB_O) * ROWB;
+      const s16x4 lo = lds_read_tr16(lv, a0);
+      const s16x4 hi = lds_read_tr16(lv, a0 + 8 * ROWB);
+      const op8 va = __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[j % MB_O] = M::mma(va, pb[j / MB_O], o[j % MB_O]);
+    }
+  };
+  if (w < ntile) load_tile(std::integral_constant<int, 0>{}, w);
+  for (int t = w; t < ntile; t += 8) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 4 < ntile) step(std::integral_constant<int, 1>{}, t + 4);
+  }
+
+  // merge the 4 waves' states per head through LDS (the V buffers are free now)
+  const float l_tot = pair_sum(l_run);
+  __syncthreads();
+  float* so = reinterpret_cast<float*>(&vbuf[0][0][0]);  // [wave][head][d]
+  if (l32 < HG) {
+#pragma unroll
+    for (int mb = 0; mb < MB_O; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) so[(w * HG + l32) * D + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3)] = o[mb][i];
+    if (h == 0) {
+      mst[w][l32] = m_run;
+      lst[w][l32] = l_tot;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < HG * D; idx += 256) {
+    const int g = idx / D, d = idx - g * D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Mx = fmaxf(Mx, mst[v][g]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float wgt = mst[v][g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mst[v][g] - Mx);
+      L = fmaf(lst[v][g], wgt, L);
+      acc = fmaf(so[(v * HG + g) * D + d], wgt, acc);
+    }
+    const size_t ps = (size_t)(bh0 + g) * splits + split;
+    Opart[ps * D + d] = acc / L;
+    if (d == 0) Lpart[ps] = (Mx + __log2f(L)) * kLn2;
+  }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ Opart,
                                                          const float* __restrict__ Lpart,
@@ -213,9 +398,22 @@ hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* ou
                            int Hkv, int Nk, float scale, int splits, void* workspace, hipStream_t stream) {
   float* opart = static_cast<float*>(workspace);
   float* lpart = opart + (size_t)B * H * splits * D;
-  hipLaunchKernelGGL((decode_partial_kernel<D, BF16, HG>), dim3(B * H / HG * splits), dim3(kDecThreads), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits, H, H / Hkv);
+  // 4 or 8 heads per K/V head go to the matrix cores (32-bit buffer offsets
+  // within one head's K/V)
+  if constexpr (HG >= 4) {
+    if ((long long)Nk * D * 2 <= 0xFFFFFFFFll)
+      hipLaunchKernelGGL((decode_mfma_kernel<D, BF16, HG>), dim3(B * H / HG * splits), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits, H, H / Hkv);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<D, BF16, HG>), dim3(B * H / HG * splits), dim3(kDecThreads), 0,
+                         stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits, H, H / Hkv);
+  } else {
+    hipLaunchKernelGGL((decode_partial_kernel<D, BF16, HG>), dim3(B * H / HG * splits), dim3(kDecThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits, H, H / Hkv);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, BF16>), dim3(B * H), dim3(D), 0, stream, opart, lpart,
