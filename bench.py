@@ -277,6 +277,7 @@ def main():
     ap.add_argument("--mfma-from", metavar="DIR")
     ap.add_argument("--decode-traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--quant-only", action="store_true")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from(*args.traffic_from)))
@@ -312,6 +313,19 @@ def main():
         _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, scale=wd.scale, out=o, lse=l, workspace=ws)],
                                 args.steps, args.warmup)
         print(json.dumps({"workload": "decode_8k", "ms": round(per[0] * 1e3, 4)}))
+        return
+    if args.quant_only:
+        # the quantised forward of quant_8k alone (int8 scores, E4M3 P.V; for its counter runs)
+        wq = G.WORKLOADS["quant_8k"]
+        tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(wq, threads=16))
+        q8, sq = F.quantize_rows_i8(tq)
+        k8, sk = F.quantize_rows_i8(tk)
+        v8, sv = F.quantize_tensor_e4m3(tv)
+        o = torch.empty((wq.B, wq.H, wq.Nq, wq.d), device="cuda", dtype=torch.bfloat16)
+        l = torch.empty((wq.B, wq.H, wq.Nq), device="cuda")
+        _, per = timed_launches([lambda: F.attn_fwd_q8(q8, k8, v8, sq, sk, sv, scale=wq.scale, out=o, lse=l)],
+                                args.steps, args.warmup)
+        print(json.dumps({"workload": "quant_8k", "ms": round(per[0] * 1e3, 4)}))
         return
     w = G.WORKLOADS["prefill_4k"]
     q, k, v = (G.to_torch(x, "bf16") for x in G.draw_qkv(w, threads=16))
