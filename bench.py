@@ -62,7 +62,7 @@ PEAK_FP8_TFLOPS = 5000.0      # dense fp8 / int8
 PEAK_HBM_GBS = 8000.0         # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4k_traffic.json")
 COPY_BYTES = 1 << 30          # bytes read (and written) by one calibration copy
-PREFILL_KERNEL = "prefill_kernel<128, true, false>"   # bf16, non-causal
+PREFILL_KERNEL = "prefill_kernel<128, true, false, 0>"   # bf16, non-causal, all exp2 on v_exp_f32
 MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_4k_mfma.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8k_traffic.json")
 DECODE_KERNELS = ("decode_partial_kernel<128, true, 1>", "decode_merge_kernel")
@@ -390,6 +390,16 @@ def main():
         # products (Q K^T, P^T dO, dO V^T, dS K, dS^T Q) = 2.5x the forward's
         tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(w, threads=16))
         tdo = G.to_torch(G.draw_tensor(w, "do", threads=16), "bf16")
+        # the software-exp2 split (2 or 4 of every 8 softmax exponentials on the
+        # library's polynomial instead of v_exp_f32), non-causal, beside the default
+        so, sl = torch.empty_like(tq), torch.empty((w.B, w.H, w.Nq), device="cuda")
+        _, pers = timed_launches([lambda sh=sh: F.attn_fwd_exp2_split(tq, tk, tv, sh, causal=False, scale=w.scale,
+                                                                      out=so, lse=sl) for sh in (0, 2, 4)],
+                                 max(5, args.steps // 2), args.warmup)
+        other["prefill_4k_exp2_split"] = {
+            "ms_by_poly_share": {f"{sh}/8": round(t * 1e3, 4) for sh, t in zip((0, 2, 4), pers)},
+            "tflops_by_poly_share": {f"{sh}/8": round(flops_nc / t / 1e12, 3) for sh, t in zip((0, 2, 4), pers)}}
+        del so, sl
         dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
         ws = torch.empty(w.B * w.H * w.Nq * 8, device="cuda", dtype=torch.uint8)
         for causal in (False, True):

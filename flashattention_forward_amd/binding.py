@@ -43,6 +43,8 @@ SIGNATURES = {
     "attn_rotate_quantize_e4m3": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "attn_fwd_fp4p": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_debug_cvt_e2m1": (_I, [_P, _P, _L, _P]),
+    "attn_fwd_exp2_split": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "attn_debug_exp2_poly": (_I, [_P, _P, _L, _P]),
     "attn_debug_qk_i32": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_debug_qk_f8": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_debug_cvt_e4m3": (_I, [_P, _P, _L, _P]),
@@ -432,4 +434,31 @@ def debug_cvt_e4m3(x):
     torch = _torch()
     y = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
     _check(lib().attn_debug_cvt_e4m3(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream()), "attn_debug_cvt_e4m3")
+    return y
+
+
+def attn_fwd_exp2_split(q, k, v, poly_per_8: int, causal: bool = False, scale: float | None = None, out=None,
+                        lse=None):
+    """The dense prefill with poly_per_8 (0, 2 or 4) of every 8 softmax
+    exponentials on the library's polynomial exp2 (d = 128 for 2 and 4).
+    q, k, v [B, H, N, d] bf16/fp16.  Returns (O, LSE)."""
+    torch = _torch()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d] of one dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check(lib().attn_fwd_exp2_split(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
+                                     B, H, Nq, Nk, d, scale, int(bool(causal)), _dtype_code(q), int(poly_per_8),
+                                     _stream()), "attn_fwd_exp2_split")
+    return out, lse
+
+
+def debug_exp2_poly(x):
+    """The library's polynomial exp2 at every element of an fp32 GPU tensor."""
+    torch = _torch()
+    y = torch.empty(x.shape, device=x.device, dtype=torch.float32)
+    _check(lib().attn_debug_exp2_poly(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream()), "attn_debug_exp2_poly")
     return y

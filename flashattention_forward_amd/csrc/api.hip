@@ -314,6 +314,30 @@ int attn_debug_cvt_e2m1(const float* x, uint8_t* y, long n, void* stream) {
   return hip_status(attn::launch_debug_cvt_e2m1(x, y, n, static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_exp2_split(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq,
+                        int Nk, int d, float scale, int causal, int dtype, int poly_per_8, void* stream) {
+  const int rc = check_common(q, k, v, out, lse, B, H, Nq, Nk, scale, causal);
+  if (rc != ATTN_OK) return rc;
+  if (poly_per_8 != 0 && poly_per_8 != 2 && poly_per_8 != 4) return ATTN_E_INVALID;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (poly_per_8 != 0 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (!prefill_head_ok(Nq, Nk, d)) return ATTN_E_INVALID;
+  const attn::SeqShape sh{nullptr, nullptr, H, 1, Nq, Nk};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (poly_per_8 == 0)
+    return hip_status(attn::launch_prefill(q, k, v, out, lse, sh, B, Nq, d, scale, causal != 0, dtype == ATTN_BF16, st));
+  return hip_status(attn::launch_prefill_exp2_split(q, k, v, out, lse, sh, B, Nq, d, scale, causal != 0,
+                                                    dtype == ATTN_BF16, poly_per_8, st));
+}
+
+int attn_debug_exp2_poly(const float* x, float* y, long n, void* stream) {
+  if (!x || !y || n < 1) return ATTN_E_INVALID;
+  if (!aligned4(x) || !aligned4(y)) return ATTN_E_INVALID;
+  if ((n + 255) / 256 > INT_MAX) return ATTN_E_INVALID;
+  return hip_status(attn::launch_debug_exp2_poly(x, y, n, static_cast<hipStream_t>(stream)));
+}
+
 int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream) {
   if (!x || !y || n < 2 || n % 2) return ATTN_E_INVALID;
   if (!aligned4(x)) return ATTN_E_INVALID;

@@ -61,5 +61,11 @@ hipError_t launch_debug_qk(const void* q8, const void* k8, void* s, int Nq, int 
                            hipStream_t stream);
 hipError_t launch_debug_cvt_e4m3(const float* x, uint8_t* y, long n, hipStream_t stream);
 hipError_t launch_debug_cvt_e2m1(const float* x, uint8_t* y, long n, hipStream_t stream);
+// the d = 128 prefill with poly_per_8 (2 or 4) of every 8 softmax exponentials
+// on the FMA-pipe polynomial; its evaluation hook
+hipError_t launch_prefill_exp2_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                                     const SeqShape& sh, int nseq, int max_nq, int d, float scale, bool causal, bool bf16,
+                                     int poly_per_8, hipStream_t stream);
+hipError_t launch_debug_exp2_poly(const float* x, float* y, long n, hipStream_t stream);
 
 }  // namespace attn

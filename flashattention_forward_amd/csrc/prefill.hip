@@ -82,6 +82,27 @@ __device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
+// exp2 on the FMA pipe, for the software-exp2 split of "Software exp2" in the
+// linux-konsole.com post "FlashAttention 4: fast, memory-efficient attention
+// for LLMs" (a share of the exponentials computed by a polynomial instead of
+// the transcendental unit).  Range reduction 2^x = 2^n 2^f with n = floor(x),
+// f = x - n in [0, 1) (exact in fp32), a cubic for 2^f, and 2^n added to the
+// exponent field.  The cubic is our relative-error minimax fit of 2^f on
+// [0, 1] (Remez exchange; flashattention_forward_amd/exp2_poly_fit.py
+// reproduces these fp32 coefficients); its relative error is at most 7.5e-5,
+// and arguments below -125 (masked keys, -inf) give 0; from -125 up every
+// result is a normal fp32 number, so adding n to the exponent field is exact.
+constexpr float kExp2C0 = 0.9999251961708069f, kExp2C1 = 0.6958335638046265f, kExp2C2 = 0.22606715559959412f,
+                kExp2C3 = 0.07802452147006989f;
+__device__ __forceinline__ float exp2_poly(float x) {
+  const float xc = fmaxf(x, -125.f);
+  const float n = floorf(xc);
+  const float f = xc - n;
+  const float p = fmaf(fmaf(fmaf(kExp2C3, f, kExp2C2), f, kExp2C1), f, kExp2C0);
+  const float r = __builtin_bit_cast(float, __builtin_bit_cast(int, p) + ((int)n << 23));
+  return x < -125.f ? 0.f : r;
+}
+
 // Raise the running max only when a tile exceeds it by more than this
 // (log2 units): P = exp2(s - m) then stays below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
@@ -102,7 +123,9 @@ __device__ __forceinline__ void tile_load_lds(const __amdgpu_buffer_rsrc_t& r, c
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)dst, 16, voff, 0, 0, 0);
 }
 
-template <int D, bool BF16, bool CAUSAL>
+// SWX: how many of every 8 exponentials of the softmax take exp2_poly (the
+// rest take v_exp_f32); 0 in the default forward
+template <int D, bool BF16, bool CAUSAL, int SWX>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, SeqShape sh, float c, int nqb, int total, int paired,
@@ -334,8 +357,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
           op2 pr[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j], c, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use));
+            const float x0 = fmaf(s[nb][8 * tt + 2 * j], c, -m_use);
+            const float x1 = fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use);
+            const float p0 = 2 * j < SWX ? exp2_poly(x0) : __builtin_amdgcn_exp2f(x0);
+            const float p1 = 2 * j + 1 < SWX ? exp2_poly(x1) : __builtin_amdgcn_exp2f(x1);
             pr[j] = M::pack2(p0, p1);
             lsum[j] += p0 + p1;
           }
@@ -422,7 +447,7 @@ static int device_cu_count() {
   return n;
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, int SWX = 0>
 static hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse, const SeqShape& sh,
                            int nseq, int max_nq, float scale, hipStream_t stream) {
   using C = PrefillCfg<D>;
@@ -440,7 +465,7 @@ static hipError_t launch_t(const void* q, const void* k, const void* v, void* ou
   const int cus = device_cu_count() & ~7;
   const int persist = (sh.cu_q == nullptr && (!CAUSAL || paired) && cus >= 8 && total > cus) ? 1 : 0;
   const int grid = persist ? cus : total;
-  hipLaunchKernelGGL((prefill_kernel<D, BF16, CAUSAL>), dim3(grid), dim3(C::NT), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, BF16, CAUSAL, SWX>), dim3(grid), dim3(C::NT), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, sh, scale * kLog2e, nqb,
                      total, paired, persist);
@@ -462,6 +487,35 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* out
   ATTN_DISPATCH(64, false, true)
 #undef ATTN_DISPATCH
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_exp2_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                                     const SeqShape& sh, int nseq, int max_nq, int d, float scale, bool causal, bool bf16,
+                                     int poly_per_8, hipStream_t stream) {
+#define ATTN_DISPATCH(BF_, CA_, SW_)                                      \
+  if (d == 128 && bf16 == BF_ && causal == CA_ && poly_per_8 == SW_) \
+    return launch_t<128, BF_, CA_, SW_>(q, k, v, out, lse, sh, nseq, max_nq, scale, stream);
+  ATTN_DISPATCH(true, false, 2)
+  ATTN_DISPATCH(true, true, 2)
+  ATTN_DISPATCH(false, false, 2)
+  ATTN_DISPATCH(false, true, 2)
+  ATTN_DISPATCH(true, false, 4)
+  ATTN_DISPATCH(true, true, 4)
+  ATTN_DISPATCH(false, false, 4)
+  ATTN_DISPATCH(false, true, 4)
+#undef ATTN_DISPATCH
+  return hipErrorInvalidValue;
+}
+
+// y[i] = exp2_poly(x[i]): the polynomial exactly as the split softmax uses it
+__global__ void debug_exp2_poly_kernel(const float* __restrict__ x, float* __restrict__ y, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = exp2_poly(x[i]);
+}
+
+hipError_t launch_debug_exp2_poly(const float* x, float* y, long n, hipStream_t stream) {
+  hipLaunchKernelGGL(debug_exp2_poly_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, y, n);
+  return hipGetLastError();
 }
 
 }  // namespace attn

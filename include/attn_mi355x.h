@@ -345,6 +345,26 @@ int attn_debug_qk_f8(const uint8_t* q8, const uint8_t* k8, float* s, int Nq, int
 int attn_debug_cvt_e4m3(const float* x, uint8_t* y, long n, void* stream);
 int attn_debug_cvt_e2m1(const float* x, uint8_t* y, long n, void* stream);
 
+/*
+ * Software-exp2 split ("Software exp2" in the linux-konsole.com post
+ * "FlashAttention 4: fast, memory-efficient attention for LLMs": part of the
+ * softmax's exponentials computed by a polynomial on the FMA units instead of
+ * the transcendental unit).  attn_fwd_exp2_split is the dense prefill of
+ * attn_fwd (Hkv = H, any Nq >= 1, the same layouts, scale, causal rule and
+ * errors) with poly_per_8 of every 8 exponentials on the polynomial:
+ *   poly_per_8 in {0, 2, 4}; 0 is attn_fwd's prefill kernel itself;
+ *   2 and 4 need d == 128 (ATTN_E_UNSUPPORTED otherwise).
+ * The polynomial is 2^x = 2^floor(x) * c(x - floor(x)) with a cubic c fitted
+ * for relative error (at most 7.5e-5); arguments below -125 give 0.  On
+ * gfx950 v_exp_f32 costs about two FMAs, so the split is slower than the
+ * default; it is kept to measure that.
+ * attn_debug_exp2_poly: y[i] = that polynomial at x[i] (fp32 device arrays,
+ *   n >= 1), the routine the split softmax calls.
+ */
+int attn_fwd_exp2_split(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq,
+                        int Nk, int d, float scale, int causal, int dtype, int poly_per_8, void* stream);
+int attn_debug_exp2_poly(const float* x, float* y, long n, void* stream);
+
 /* Static text for a return code. */
 const char* attn_status_str(int status);
 

@@ -235,3 +235,25 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(Bd, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         Bd.lib()
+
+
+def test_exp2_split_rejects():
+    """The software-exp2 split prefill: shares other than 0, 2, 4 are invalid;
+    shares 2 and 4 need d = 128; otherwise attn_fwd's checks apply."""
+    L = Bd.lib()
+    sp = lambda **kw: L.attn_fwd_exp2_split(kw.get("q", A), A, A, A, kw.get("lse", A), 1, 1, kw.get("Nq", 8), 8,
+                                            kw.get("d", 128), kw.get("scale", 0.1), kw.get("causal", 0),
+                                            kw.get("dtype", Bd.ATTN_BF16), kw.get("poly", 2), None)
+    assert sp(poly=3) == Bd.ATTN_E_INVALID
+    assert sp(poly=8) == Bd.ATTN_E_INVALID
+    assert sp(poly=-2) == Bd.ATTN_E_INVALID
+    assert sp(d=64) == Bd.ATTN_E_UNSUPPORTED
+    assert sp(d=96, poly=0) == Bd.ATTN_E_UNSUPPORTED
+    assert sp(dtype=5) == Bd.ATTN_E_UNSUPPORTED
+    assert sp(q=MIS) == Bd.ATTN_E_INVALID
+    assert sp(lse=A + 2) == Bd.ATTN_E_INVALID
+    assert sp(Nq=9, causal=1) == Bd.ATTN_E_INVALID
+    assert sp(scale=float("nan")) == Bd.ATTN_E_INVALID
+    assert L.attn_debug_exp2_poly(A, A, 0, None) == Bd.ATTN_E_INVALID
+    assert L.attn_debug_exp2_poly(None, A, 8, None) == Bd.ATTN_E_INVALID
+    assert L.attn_debug_exp2_poly(A + 2, A, 8, None) == Bd.ATTN_E_INVALID
