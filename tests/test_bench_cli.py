@@ -1,0 +1,43 @@
+"""bench.py on the CPU: its one-GPU contract and the freshness of the counter
+records it reports.
+
+* ``--gpus`` above 1 exits with status 2 and a message that says there is no
+  multi-GPU path (nothing is launched).
+* The committed rocprofv3 records (prefill HBM traffic, prefill MFMA
+  utilisation, decode HBM bytes) were taken on the kernel code now in the
+  tree.  Each record carries a hash of its kernel's sources, comments and
+  blank space removed.  A stale record makes the bench report its traffic as
+  null, so a kernel change must come with new counter runs.
+* A record whose hash does not match is refused."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_committed_counter_records_are_current():
+    assert bench._current_record(bench.TRAFFIC_FILE) is not None, "prefill traffic record is stale"
+    assert bench._current_record(bench.MFMA_FILE) is not None, "prefill MFMA record is stale"
+    assert bench._current_record(bench.DECODE_TRAFFIC_FILE, bench.DECODE_SOURCES) is not None, \
+        "decode traffic record is stale"
+    assert bench.traffic_per_launch() is not None
+
+
+def test_stale_record_is_refused(tmp_path):
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    rec["kernel_source_sha"] = "0" * 16
+    p = tmp_path / "stale.json"
+    p.write_text(json.dumps(rec))
+    assert bench._current_record(str(p)) is None
+    assert bench._current_record(str(tmp_path / "missing.json")) is None
