@@ -100,6 +100,10 @@ def _dev(t, name):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    cur = _torch().cuda.current_device()
+    if t.device.index != cur:
+        # the library launches on the current device's stream
+        raise ValueError(f"{name} is on {t.device} but the current device is cuda:{cur}")
     return ctypes.c_void_p(t.data_ptr())
 
 
