@@ -116,11 +116,53 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _need(t, name, shape=None, dtype=None, numel=None):
+    """Shape, dtype and size checks of a caller's tensor, before any pointer
+    is taken: the kernels read and write through raw pointers sized by the
+    other arguments, so a mismatched tensor would be accessed out of bounds."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_workspace(ws, need: int, name: str = "workspace"):
+    if ws is not None and _nbytes(ws) < need:
+        raise ValueError(f"{name} holds {_nbytes(ws)} bytes, {need} needed")
+    return ws
+
+
+def _need_offsets(cu_q, cu_k):
+    """Packed-batch offsets: int32, one dimension, nseq + 1 >= 2 entries each."""
+    torch = _torch()
+    for t, name in ((cu_q, "cu_seqlens_q"), (cu_k, "cu_seqlens_k")):
+        if t.dtype != torch.int32 or t.dim() != 1 or t.numel() < 2:
+            raise ValueError(f"{name} must be a 1-D int32 tensor of nseq + 1 >= 2 offsets")
+    if cu_k.numel() != cu_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    return cu_q.numel() - 1
+
+
 def workspace_bytes(B, H, Nq, Nk, d, dtype_code, Hkv=None) -> int:
     """Workspace attn_fwd needs (nonzero only for Nq == 1); Hkv < H for grouped-query heads."""
     if Hkv is None or Hkv == H:
         return int(lib().attn_fwd_workspace_bytes(B, H, Nq, Nk, d, dtype_code))
     return int(lib().attn_fwd_gqa_workspace_bytes(B, H, Hkv, Nq, Nk, d, dtype_code))
+
+
+def _dims(t, name, nd):
+    if t.dim() != nd:
+        raise ValueError(f"{name} must have {nd} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -129,8 +171,8 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     k and v may have fewer heads than q (grouped-query attention: query head
     h reads K/V head h // (H // Hkv))."""
     torch = _torch()
-    B, H, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, H, Nq, d = _dims(q, "q", 4)
+    Hkv, Nk = _dims(k, "k", 4)[1], k.shape[2]
     if k.shape != (B, Hkv, Nk, d) or v.shape != (B, Hkv, Nk, d):
         raise ValueError("q must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
     if not (q.dtype == k.dtype == v.dtype):
@@ -139,14 +181,18 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, "out", q.shape, q.dtype)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _need(lse, "lse", numel=B * H * Nq, dtype=torch.float32)
     wsb = workspace_bytes(B, H, Nq, Nk, d, code, Hkv)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
+    _need_workspace(workspace, wsb)
     args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None]
     tail = [d, scale, int(bool(causal)), code, _dev(workspace, "workspace") if workspace is not None else None,
-            workspace.numel() if workspace is not None else 0, _stream()]
+            _nbytes(workspace) if workspace is not None else 0, _stream()]
     if Hkv == H:
         rc = lib().attn_fwd(*args, B, H, Nq, Nk, *tail)
         _check(rc, "attn_fwd")
@@ -162,22 +208,22 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     cu_seqlens_* int32 GPU tensors of nseq + 1 offsets.  Returns (out, lse)
     with lse [H, total_q]."""
     torch = _torch()
-    H, total_q, d = q.shape
-    Hkv, total_k = k.shape[0], k.shape[1]
+    H, total_q, d = _dims(q, "q", 3)
+    Hkv, total_k = _dims(k, "k", 3)[0], k.shape[1]
     if k.shape != (Hkv, total_k, d) or v.shape != (Hkv, total_k, d):
         raise ValueError("q must be [H, total_q, d] and k, v [Hkv, total_k, d]")
-    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be int32")
-    nseq = cu_seqlens_q.numel() - 1
-    if cu_seqlens_k.numel() != nseq + 1:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    nseq = _need_offsets(cu_seqlens_q, cu_seqlens_k)
+    code = _dtype_code(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((H, total_q), device=q.device, dtype=torch.float32) if lse is None else lse
+    out = torch.empty_like(q) if out is None else _need(out, "out", q.shape, q.dtype)
+    lse = (torch.empty((H, total_q), device=q.device, dtype=torch.float32) if lse is None
+           else _need(lse, "lse", numel=H * total_q, dtype=torch.float32))
     rc = lib().attn_fwd_varlen(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
                                _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), nseq,
                                int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, H, Hkv, d, scale,
-                               int(bool(causal)), _dtype_code(q), _stream())
+                               int(bool(causal)), code, _stream())
     _check(rc, "attn_fwd_varlen")
     return out, lse
 
@@ -187,8 +233,8 @@ def attn_bwd(q, k, v, out, dout, lse, causal: bool = False, scale: float | None 
     """dQ, dK, dV of sum(dout * out) for out, lse = attn_fwd(q, k, v, causal, scale).
     k, v may have fewer heads than q (grouped-query attention)."""
     torch = _torch()
-    B, H, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, H, Nq, d = _dims(q, "q", 4)
+    Hkv, Nk = _dims(k, "k", 4)[1], k.shape[2]
     if k.shape != (B, Hkv, Nk, d) or v.shape != (B, Hkv, Nk, d) or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("q, out, dout must be [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
     if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
@@ -197,15 +243,16 @@ def attn_bwd(q, k, v, out, dout, lse, causal: bool = False, scale: float | None 
         raise ValueError("lse must be the [B, H, Nq] float32 log-sum-exp of the forward")
     code = _dtype_code(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _need(dq, "dq", q.shape, q.dtype)
+    dk = torch.empty_like(k) if dk is None else _need(dk, "dk", k.shape, k.dtype)
+    dv = torch.empty_like(v) if dv is None else _need(dv, "dv", v.shape, v.dtype)
     wsb = int(lib().attn_bwd_workspace_bytes(B, H, Nq, Nk, d, code))
     if workspace is None:
         workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
+    _need_workspace(workspace, wsb)
     args = [_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"), _dev(lse, "lse"),
             _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv")]
-    tail = [d, scale, int(bool(causal)), code, _dev(workspace, "workspace"), workspace.numel(), _stream()]
+    tail = [d, scale, int(bool(causal)), code, _dev(workspace, "workspace"), _nbytes(workspace), _stream()]
     if Hkv == H:
         _check(lib().attn_bwd(*args, B, H, Nq, Nk, *tail), "attn_bwd")
     else:
@@ -217,24 +264,29 @@ def attn_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seq
                     causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None, workspace=None):
     """Gradients for attn_fwd_varlen (same packed layouts)."""
     torch = _torch()
-    H, total_q, d = q.shape
-    Hkv, total_k = k.shape[0], k.shape[1]
+    H, total_q, d = _dims(q, "q", 3)
+    Hkv, total_k = _dims(k, "k", 3)[0], k.shape[1]
     if k.shape != (Hkv, total_k, d) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("q, out, dout must be [H, total_q, d] and k, v [Hkv, total_k, d]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise ValueError("q, k, v, out, dout must share one dtype")
     if lse is None or lse.shape != (H, total_q) or lse.dtype != torch.float32:
         raise ValueError("lse must be the [H, total_q] float32 log-sum-exp of attn_fwd_varlen")
-    nseq = cu_seqlens_q.numel() - 1
+    nseq = _need_offsets(cu_seqlens_q, cu_seqlens_k)
+    code = _dtype_code(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _need(dq, "dq", q.shape, q.dtype)
+    dk = torch.empty_like(k) if dk is None else _need(dk, "dk", k.shape, k.dtype)
+    dv = torch.empty_like(v) if dv is None else _need(dv, "dv", v.shape, v.dtype)
+    wsb = max(16, H * total_q * 8)
     if workspace is None:
-        workspace = torch.empty(max(16, H * total_q * 8), device=q.device, dtype=torch.uint8)
+        workspace = torch.empty(wsb, device=q.device, dtype=torch.uint8)
+    _need_workspace(workspace, H * total_q * 8)
     rc = lib().attn_bwd_varlen(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
                                _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"),
                                _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), nseq,
                                int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, H, Hkv, d, scale,
-                               int(bool(causal)), _dtype_code(q), _dev(workspace, "workspace"), workspace.numel(),
+                               int(bool(causal)), code, _dev(workspace, "workspace"), _nbytes(workspace),
                                _stream())
     _check(rc, "attn_bwd_varlen")
     return dq, dk, dv
@@ -244,23 +296,36 @@ def decode_splits(B, H, Nk, d) -> int:
     return int(lib().attn_fwd_decode_splits(B, H, Nk, d))
 
 
+def _decode_shapes(q, k, v, out, lse):
+    """Shapes of a split-KV decode call: q, out [B, H, 1, d], k, v [B, H, Nk, d]."""
+    torch = _torch()
+    B, H, Nq, d = _dims(q, "q", 4)
+    if Nq != 1:
+        raise ValueError("decode takes one query per (batch, head)")
+    Nk = _dims(k, "k", 4)[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] for q [B, H, 1, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    out = torch.empty_like(q) if out is None else _need(out, "out", q.shape, q.dtype)
+    lse = (torch.empty((B, H, 1), device=q.device, dtype=torch.float32) if lse is None
+           else _need(lse, "lse", numel=B * H, dtype=torch.float32))
+    return B, H, Nk, d, code, out, lse
+
+
 def attn_fwd_decode(q, k, v, num_splits: int, scale: float | None = None, out=None, lse=None, workspace=None):
     """Split-KV decode: q [B, H, 1, d] against k, v [B, H, Nk, d]."""
     torch = _torch()
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if Nq != 1:
-        raise ValueError("decode takes one query per (batch, head)")
-    code = _dtype_code(q)
+    B, H, Nk, d, code, out, lse = _decode_shapes(q, k, v, out, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, 1), device=q.device, dtype=torch.float32) if lse is None else lse
     wsb = int(lib().attn_decode_workspace_bytes(B, H, d, num_splits))
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), device=q.device, dtype=torch.uint8)
+    _need_workspace(workspace, wsb)
     rc = lib().attn_fwd_decode(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
                                B, H, Nk, d, scale, code, num_splits, _dev(workspace, "workspace"),
-                               workspace.numel(), _stream())
+                               _nbytes(workspace), _stream())
     _check(rc, "attn_fwd_decode")
     return out, lse
 
@@ -290,10 +355,40 @@ def quantize_tensor_e4m3(x, workspace=None):
     wsb = int(lib().attn_quantize_e4m3_workspace_bytes(n))
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), device=x.device, dtype=torch.uint8)
+    _need_workspace(workspace, wsb)
     _check(lib().attn_quantize_tensor_e4m3(_dev(x, "x"), _dev(x8, "x8"), _dev(s, "scale"), n,
-                                           _dev(workspace, "workspace"), workspace.numel(), _stream()),
+                                           _dev(workspace, "workspace"), _nbytes(workspace), _stream()),
            "attn_quantize_tensor_e4m3")
     return x8, s
+
+
+def _quant_shapes(q8, k8, v8, q_scale, k_scale, v_scale, qk_dtype, v_dtype, out, lse):
+    """Shapes and dtypes of a quantised forward: q8 [B, H, Nq, d], k8, v8
+    [B, H, Nk, d], q_scale B*H*Nq, k_scale B*H*Nk, v_scale one float32."""
+    torch = _torch()
+    B, H, Nq, d = _dims(q8, "q8", 4)
+    Nk = _dims(k8, "k8", 4)[2]
+    _need(q8, "q8", dtype=qk_dtype)
+    _need(k8, "k8", (B, H, Nk, d), qk_dtype)
+    _need(v8, "v8", (B, H, Nk, d), v_dtype)
+    _need(q_scale, "q_scale", numel=B * H * Nq, dtype=torch.float32)
+    _need(k_scale, "k_scale", numel=B * H * Nk, dtype=torch.float32)
+    _need(v_scale, "v_scale", numel=1, dtype=torch.float32)
+    out = (torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None
+           else _need(out, "out", (B, H, Nq, d), torch.bfloat16))
+    lse = (torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None
+           else _need(lse, "lse", numel=B * H * Nq, dtype=torch.float32))
+    return B, H, Nq, Nk, d, out, lse
+
+
+def _quant_call(name, q8, k8, v8, q_scale, k_scale, v_scale, qk_dtype, v_dtype, causal, scale, out, lse):
+    B, H, Nq, Nk, d, out, lse = _quant_shapes(q8, k8, v8, q_scale, k_scale, v_scale, qk_dtype, v_dtype, out, lse)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = getattr(lib(), name)(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
+                              _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"),
+                              _dev(lse, "lse"), B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
+    _check(rc, name)
+    return out, lse
 
 
 def attn_fwd_q8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
@@ -301,16 +396,8 @@ def attn_fwd_q8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, sca
     """Quantised forward: int8 q8/k8 [B,H,N,d] with per-token scales, E4M3 v8 with a
     per-tensor scale (1-element GPU tensor).  Returns (O bf16, LSE fp32)."""
     torch = _torch()
-    B, H, Nq, d = q8.shape
-    Nk = k8.shape[2]
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
-    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
-    rc = lib().attn_fwd_q8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
-                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
-                           B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
-    _check(rc, "attn_fwd_q8")
-    return out, lse
+    return _quant_call("attn_fwd_q8", q8, k8, v8, q_scale, k_scale, v_scale, torch.int8, torch.uint8, causal,
+                       scale, out, lse)
 
 
 def quantize_tensor_i8(x, workspace=None):
@@ -324,8 +411,9 @@ def quantize_tensor_i8(x, workspace=None):
     wsb = int(lib().attn_quantize_e4m3_workspace_bytes(n))
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), device=x.device, dtype=torch.uint8)
+    _need_workspace(workspace, wsb)
     _check(lib().attn_quantize_tensor_i8(_dev(x, "x"), _dev(x8, "x8"), _dev(s, "scale"), n,
-                                         _dev(workspace, "workspace"), workspace.numel(), _stream()),
+                                         _dev(workspace, "workspace"), _nbytes(workspace), _stream()),
            "attn_quantize_tensor_i8")
     return x8, s
 
@@ -335,16 +423,8 @@ def attn_fwd_i8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, sca
     """All-INT8 forward: int8 q8/k8 [B,H,N,d] with per-token scales, int8 v8 with a
     per-tensor scale (1-element GPU tensor).  Returns (O bf16, LSE fp32)."""
     torch = _torch()
-    B, H, Nq, d = q8.shape
-    Nk = k8.shape[2]
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
-    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
-    rc = lib().attn_fwd_i8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
-                           _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
-                           B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
-    _check(rc, "attn_fwd_i8")
-    return out, lse
+    return _quant_call("attn_fwd_i8", q8, k8, v8, q_scale, k_scale, v_scale, torch.int8, torch.int8, causal,
+                       scale, out, lse)
 
 
 def rotate_quantize_e4m3(x, signs=None, block_rows: int = 64):
@@ -354,14 +434,15 @@ def rotate_quantize_e4m3(x, signs=None, block_rows: int = 64):
     torch = _torch()
     if x.dtype != torch.bfloat16:
         raise ValueError("rotate_quantize_e4m3 takes bf16")
+    if x.dim() < 2:
+        raise ValueError("rotate_quantize_e4m3 takes a [..., N, d] tensor")
     *lead, N, d = x.shape
     BH = int(math.prod(lead)) if lead else 1
     x8 = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
     sc = torch.empty((*lead, N), device=x.device, dtype=torch.float32)
     sp = None
     if signs is not None:
-        if signs.dtype != torch.float32 or signs.numel() != d:
-            raise ValueError("signs must be d float32 values")
+        _need(signs, "signs", numel=d, dtype=torch.float32)
         sp = _dev(signs, "signs")
     _check(lib().attn_rotate_quantize_e4m3(_dev(x, "x"), sp, _dev(x8, "x8"), _dev(sc, "scales"), BH, N, d,
                                            int(block_rows), _stream()), "attn_rotate_quantize_e4m3")
@@ -374,16 +455,8 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, sc
     rotate_quantize_e4m3), E4M3 v8 with a per-tensor scale (1-element GPU
     tensor).  Returns (O bf16, LSE fp32)."""
     torch = _torch()
-    B, H, Nq, d = q8.shape
-    Nk = k8.shape[2]
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
-    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
-    rc = lib().attn_fwd_fp8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
-                            _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
-                            B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
-    _check(rc, "attn_fwd_fp8")
-    return out, lse
+    return _quant_call("attn_fwd_fp8", q8, k8, v8, q_scale, k_scale, v_scale, torch.uint8, torch.uint8, causal,
+                       scale, out, lse)
 
 
 def attn_fwd_fp4p(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
@@ -391,43 +464,37 @@ def attn_fwd_fp4p(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, s
     """attn_fwd_fp8 with P in MXFP4 (E2M1 codes, one power-of-two scale per 32
     keys of a query).  Same arguments and results as attn_fwd_fp8."""
     torch = _torch()
-    B, H, Nq, d = q8.shape
-    Nk = k8.shape[2]
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty((B, H, Nq, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
-    lse = torch.empty((B, H, Nq), device=q8.device, dtype=torch.float32) if lse is None else lse
-    rc = lib().attn_fwd_fp4p(_dev(q8, "q8"), _dev(k8, "k8"), _dev(v8, "v8"), _dev(q_scale, "q_scale"),
-                             _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"), _dev(lse, "lse"),
-                             B, H, Nq, Nk, d, scale, int(bool(causal)), _stream())
-    _check(rc, "attn_fwd_fp4p")
-    return out, lse
+    return _quant_call("attn_fwd_fp4p", q8, k8, v8, q_scale, k_scale, v_scale, torch.uint8, torch.uint8, causal,
+                       scale, out, lse)
+
+
+def _debug_qk(name, q8, k8, code_dtype, out_dtype):
+    torch = _torch()
+    Nq, d = _dims(q8, "q8", 2)
+    Nk = _dims(k8, "k8", 2)[0]
+    _need(q8, "q8", dtype=code_dtype)
+    _need(k8, "k8", (Nk, d), code_dtype)
+    s = torch.empty((Nq, Nk), device=q8.device, dtype=out_dtype)
+    _check(getattr(lib(), name)(_dev(q8, "q8"), _dev(k8, "k8"), _dev(s, "s"), Nq, Nk, d, _stream()), name)
+    return s
 
 
 def debug_qk_i32(q8, k8):
     """int32 Q8 K8^T of one head through the quantised kernel's tile routine."""
     torch = _torch()
-    Nq, d = q8.shape
-    Nk = k8.shape[0]
-    s = torch.empty((Nq, Nk), device=q8.device, dtype=torch.int32)
-    _check(lib().attn_debug_qk_i32(_dev(q8, "q8"), _dev(k8, "k8"), _dev(s, "s"), Nq, Nk, d, _stream()),
-           "attn_debug_qk_i32")
-    return s
+    return _debug_qk("attn_debug_qk_i32", q8, k8, torch.int8, torch.int32)
 
 
 def debug_qk_f8(q8, k8):
     """fp32 scores of one head's E4M3 codes through the fp8 kernel's tile routine."""
     torch = _torch()
-    Nq, d = q8.shape
-    Nk = k8.shape[0]
-    s = torch.empty((Nq, Nk), device=q8.device, dtype=torch.float32)
-    _check(lib().attn_debug_qk_f8(_dev(q8, "q8"), _dev(k8, "k8"), _dev(s, "s"), Nq, Nk, d, _stream()),
-           "attn_debug_qk_f8")
-    return s
+    return _debug_qk("attn_debug_qk_f8", q8, k8, torch.uint8, torch.float32)
 
 
 def debug_cvt_e2m1(x):
     """E2M1 codes (one per byte) of an fp32 GPU tensor through the library's FP4 conversion."""
     torch = _torch()
+    _need(x, "x", dtype=torch.float32)
     y = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
     _check(lib().attn_debug_cvt_e2m1(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream()), "attn_debug_cvt_e2m1")
     return y
@@ -436,6 +503,7 @@ def debug_cvt_e2m1(x):
 def debug_cvt_e4m3(x):
     """E4M3 codes of an fp32 GPU tensor through the library's conversion routine."""
     torch = _torch()
+    _need(x, "x", dtype=torch.float32)
     y = torch.empty(x.shape, device=x.device, dtype=torch.uint8)
     _check(lib().attn_debug_cvt_e4m3(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream()), "attn_debug_cvt_e4m3")
     return y
@@ -447,15 +515,17 @@ def attn_fwd_exp2_split(q, k, v, poly_per_8: int, causal: bool = False, scale: f
     exponentials on the library's polynomial exp2 (d = 128 for 2 and 4).
     q, k, v [B, H, N, d] bf16/fp16.  Returns (O, LSE)."""
     torch = _torch()
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    B, H, Nq, d = _dims(q, "q", 4)
+    Nk = _dims(k, "k", 4)[2]
     if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d] of one dtype")
+    code = _dtype_code(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32) if lse is None else lse
+    out = torch.empty_like(q) if out is None else _need(out, "out", q.shape, q.dtype)
+    lse = (torch.empty((B, H, Nq), device=q.device, dtype=torch.float32) if lse is None
+           else _need(lse, "lse", numel=B * H * Nq, dtype=torch.float32))
     _check(lib().attn_fwd_exp2_split(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(lse, "lse"),
-                                     B, H, Nq, Nk, d, scale, int(bool(causal)), _dtype_code(q), int(poly_per_8),
+                                     B, H, Nq, Nk, d, scale, int(bool(causal)), code, int(poly_per_8),
                                      _stream()), "attn_fwd_exp2_split")
     return out, lse
 
@@ -463,6 +533,7 @@ def attn_fwd_exp2_split(q, k, v, poly_per_8: int, causal: bool = False, scale: f
 def debug_exp2_poly(x):
     """The library's polynomial exp2 at every element of an fp32 GPU tensor."""
     torch = _torch()
+    _need(x, "x", dtype=torch.float32)
     y = torch.empty(x.shape, device=x.device, dtype=torch.float32)
     _check(lib().attn_debug_exp2_poly(_dev(x, "x"), _dev(y, "y"), x.numel(), _stream()), "attn_debug_exp2_poly")
     return y

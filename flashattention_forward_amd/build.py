@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn_mi355x.so")
-SOURCES = ["prefill.hip", "decode.hip", "quant.hip", "bwd.hip", "api.hip"]
+SOURCES = ["prefill.hip", "decode.hip", "quant.hip", "bwd.hip", "api.cpp", "plan.cpp"]
 ARCH = "gfx950"
 
 
@@ -41,7 +41,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:

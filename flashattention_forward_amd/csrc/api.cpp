@@ -1,6 +1,9 @@
 // C ABI of libattn_mi355x.so: argument validation and kernel dispatch.
-// Every check runs on the host before anything is launched; an error return
-// means no work was enqueued.  See include/attn_mi355x.h for the contract.
+// Every check runs on the host before anything is launched; a validation
+// error means no work was enqueued.  See include/attn_mi355x.h for the
+// contract.  Host-only C++: it calls the launchers declared in internal.h
+// and nothing else of HIP, so it also builds for the CPU against stub
+// launchers (the sanitizer build of the validation layer used by the tests).
 #include <cmath>
 #include <algorithm>
 #include <climits>
@@ -22,10 +25,10 @@ bool prefill_grid_ok(int B, int H, int Nq) {
   return g <= INT_MAX;
 }
 
-// the bf16/fp16 prefill addresses one head through buffer descriptors with
-// 32-bit sizes and offsets
+// the bf16/fp16 prefill and the backward address one head of Q, K, V, O
+// through buffer resources: each head spans at most kMaxSpanBytes
 bool prefill_head_ok(int Nq, int Nk, int d) {
-  return (long long)Nq * d * 2 <= (long long)UINT32_MAX && (long long)Nk * d * 2 <= (long long)UINT32_MAX;
+  return attn::span_ok((long long)Nq * d * 2) && attn::span_ok((long long)Nk * d * 2);
 }
 
 int check_common(const void* q, const void* k, const void* v, const void* out, const float* lse, int B, int H, int Nq,
@@ -164,7 +167,7 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out, c
   if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
   if (!prefill_head_ok(Nq, Nk, d) || !prefill_grid_ok(B, H, Nk)) return ATTN_E_INVALID;
-  if ((long long)Nq * 8 > (long long)UINT32_MAX) return ATTN_E_INVALID;
+  if (!attn::span_ok((long long)Nq * 8)) return ATTN_E_INVALID;  // per-row (lse, D) pairs
   const long rows = (long)B * H * Nq;
   if (!workspace || workspace_bytes < attn::bwd_workspace_bytes(rows) || !aligned16(workspace))
     return ATTN_E_WORKSPACE;
@@ -188,7 +191,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* out
   if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
   if (!prefill_head_ok(max_seqlen_q, max_seqlen_k, d) || !prefill_grid_ok(nseq, H, max_seqlen_q) ||
-      !prefill_grid_ok(nseq, H, max_seqlen_k) || (long long)max_seqlen_q * 8 > (long long)UINT32_MAX)
+      !prefill_grid_ok(nseq, H, max_seqlen_k) || !attn::span_ok((long long)max_seqlen_q * 8))
     return ATTN_E_INVALID;
   const long rows = (long)H * total_q;
   if (!workspace || workspace_bytes < attn::bwd_workspace_bytes(rows) || !aligned16(workspace))

@@ -567,17 +567,26 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   using C = BwdCfg<D>;
   float2* ld = static_cast<float2*>(workspace);
   constexpr int RPB = 256 / (D / 8);  // rows per bwd_pre block
-  hipLaunchKernelGGL((bwd_pre_kernel<D, BF16>), dim3((unsigned)((q_rows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, ld, q_rows);
+  // a packed batch may have no query rows at all (its keys still get dK = dV = 0);
+  // a grid of zero blocks is a launch error, so the preprocess is skipped then
+  if (q_rows > 0) {
+    hipLaunchKernelGGL((bwd_pre_kernel<D, BF16>), dim3((unsigned)((q_rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, ld, q_rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const float c = scale * kLog2e;
   const int nkb = (max_nk + C::BO - 1) / C::BO;
   const int totk = nkb * nseq * (sh.H / sh.group);
-  if (totk > 0)
+  if (totk > 0) {
     hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, CAUSAL>), dim3(totk), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk,
                        sh.cu_q != nullptr ? totk / nkb : max(1, totk / nkb / 8));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int nqb = (max_nq + C::BO - 1) / C::BO;
   const int totq = nqb * nseq * sh.H;
   if (totq > 0)
@@ -590,8 +599,6 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
 }
 
 }  // namespace
-
-size_t bwd_workspace_bytes(long q_rows) { return (size_t)q_rows * sizeof(float2); }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, const SeqShape& sh, int nseq, int max_nq, int max_nk, long q_rows,

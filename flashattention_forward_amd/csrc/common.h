@@ -121,6 +121,32 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100, kSchedDsWrite = 0x200,
               kSchedVmemRead = 0x020;
 
+// ---------------------------------------------------------------- sequences
+// The rows of one (sequence, head) in the dense or packed layout (SeqShape).
+struct SeqSpan {
+  size_t q_row0, k_row0;  // first Q/O/LSE row and first K/V row of the (sequence, head)
+  int nq, nk;             // its query and key counts
+};
+__device__ __forceinline__ SeqSpan seq_span(const SeqShape& a, int s, int h) {
+  SeqSpan r;
+  const int hk = h / a.group;
+  if (a.cu_q != nullptr) {
+    // offsets clamped into [0, total] and made non-decreasing, so malformed
+    // offsets can only select wrong rows of this head, never memory outside it
+    const int qa = min(max(a.cu_q[s], 0), a.Nq), ka = min(max(a.cu_k[s], 0), a.Nk);
+    r.nq = min(max(a.cu_q[s + 1], qa), a.Nq) - qa;
+    r.nk = min(max(a.cu_k[s + 1], ka), a.Nk) - ka;
+    r.q_row0 = (size_t)h * a.Nq + qa;
+    r.k_row0 = (size_t)hk * a.Nk + ka;
+  } else {
+    r.nq = a.Nq;
+    r.nk = a.Nk;
+    r.q_row0 = ((size_t)s * a.H + h) * a.Nq;
+    r.k_row0 = ((size_t)s * (a.H / a.group) + hk) * a.Nk;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- grid order
 // Workgroups are handed to the 8 XCDs round robin (id % 8).  Renumber them so
 // each XCD receives one contiguous range of logical work items; neighbouring

@@ -398,10 +398,10 @@ hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* ou
                            int Hkv, int Nk, float scale, int splits, void* workspace, hipStream_t stream) {
   float* opart = static_cast<float*>(workspace);
   float* lpart = opart + (size_t)B * H * splits * D;
-  // 4 or 8 heads per K/V head go to the matrix cores (32-bit buffer offsets
-  // within one head's K/V)
+  // 4 or 8 heads per K/V head go to the matrix cores, which address one
+  // head's K/V through buffer resources (at most kMaxSpanBytes)
   if constexpr (HG >= 4) {
-    if ((long long)Nk * D * 2 <= 0xFFFFFFFFll)
+    if (span_ok((long long)Nk * D * 2))
       hipLaunchKernelGGL((decode_mfma_kernel<D, BF16, HG>), dim3(B * H / HG * splits), dim3(256), 0, stream,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), opart, lpart, Nk, scale * kLog2e, splits, H, H / Hkv);
@@ -434,28 +434,6 @@ hipError_t launch_decode_g(const void* q, const void* k, const void* v, void* ou
 }
 
 }  // namespace
-
-size_t decode_workspace_bytes(int B, int H, int d, int splits) {
-  return (size_t)B * H * splits * (d + 1) * sizeof(float);
-}
-
-int decode_heads_per_workgroup(int H, int Hkv) {
-  const int group = H / Hkv;
-  return group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-}
-
-int decode_default_splits(int B, int H, int Hkv, int Nk, int d) {
-  (void)d;
-  // aim for about 8192 (query head, key range) streams with at least 128 keys
-  // each.  A grouped workgroup serves several heads of a range at once; counting
-  // streams per query head still measured best for it (splitting its key range
-  // further only added partial states to write and merge)
-  (void)Hkv;
-  long bh = (long)B * H;
-  int s = 1;
-  while (bh * s < 8192 && s < 256 && (long)(s * 2) * 128 <= Nk) s *= 2;
-  return s;
-}
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
                          int Nk, int d, float scale, bool bf16, int splits, void* workspace, hipStream_t stream) {

@@ -1,13 +1,30 @@
-// Host-side launchers of the gfx950 kernels, called by the C ABI in api.hip
-// after it has validated every argument.
+// Host-side launchers of the gfx950 kernels, called by the C ABI in api.cpp
+// after it has validated every argument, and the host-side sizing rules
+// (workspace sizes, split counts) in plan.cpp.  Host-only declarations: the
+// validation layer builds against this header without any device code.
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
 #include "seq_shape.h"
 
 namespace attn {
+
+// Largest byte span one buffer resource may cover.  The kernels address a
+// head of Q, K, V or O (and the backward's per-row statistics) through
+// buffer resources with 32-bit offsets, and form offsets up to one tile
+// (16 KiB; 64 KiB allowed here) past the end of a span when they prefetch a
+// tile that is then never used.  Spans of at most 2^31 - 2^16 bytes keep
+// every such offset below 2^31, so no offset wraps around and its signed
+// and unsigned readings agree.  The C ABI rejects larger heads
+// (ATTN_E_INVALID); the decode path takes its vector-ALU kernel, which
+// addresses memory through 64-bit pointers, for longer key ranges.
+constexpr long long kMaxSpanBytes = (1LL << 31) - (1LL << 16);
+inline bool span_ok(long long bytes) { return bytes >= 0 && bytes <= kMaxSpanBytes; }
+
+// Partial maxima of the two-pass per-tensor reduction over n elements.
+int e4m3_partials(long n);
 
 // Tiled prefill forward, bf16/fp16, d in {64, 128}, over nseq sequences of
 // at most max_nq queries each (see SeqShape for the layouts).

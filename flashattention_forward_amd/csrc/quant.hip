@@ -121,15 +121,7 @@ __global__ __launch_bounds__(256) void quantize_rows_i8_kernel(const uint16_t* _
 }
 
 // ------------------------------------------------------------ per-tensor E4M3
-constexpr int kMaxPartials = 1024;
-
-int e4m3_grid(long n) {
-  const long chunks = n / 8;
-  long g = (chunks + 255) / 256;
-  if (g > kMaxPartials) g = kMaxPartials;
-  if (g < 1) g = 1;
-  return (int)g;
-}
+// (the number of partial maxima, e4m3_partials(), is a host rule in plan.cpp)
 
 __global__ __launch_bounds__(256) void amax_partial_kernel(const uint16_t* __restrict__ X, long chunks,
                                                            float* __restrict__ partial) {
@@ -707,12 +699,10 @@ hipError_t launch_quantize_rows_i8(const void* x, int8_t* x8, float* scales, lon
   return hipGetLastError();
 }
 
-size_t quantize_e4m3_workspace_bytes(long n) { return (size_t)e4m3_grid(n) * sizeof(float); }
-
 hipError_t launch_quantize_tensor_e4m3(const void* x, uint8_t* x8, float* scale_out, long n, void* workspace,
                                        hipStream_t stream) {
   const long chunks = n / 8;
-  const int g = e4m3_grid(n);
+  const int g = e4m3_partials(n);
   float* partial = static_cast<float*>(workspace);
   hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(256), 0, stream, static_cast<const uint16_t*>(x), chunks,
                      partial);
@@ -765,7 +755,7 @@ hipError_t launch_rotate_quantize_e4m3(const void* x, const float* signs, uint8_
 hipError_t launch_quantize_tensor_i8(const void* x, int8_t* x8, float* scale_out, long n, void* workspace,
                                      hipStream_t stream) {
   const long chunks = n / 8;
-  const int g = e4m3_grid(n);
+  const int g = e4m3_partials(n);
   float* partial = static_cast<float*>(workspace);
   hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(256), 0, stream, static_cast<const uint16_t*>(x), chunks,
                      partial);

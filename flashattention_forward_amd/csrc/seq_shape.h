@@ -1,7 +1,8 @@
-// The dense and packed batch layouts shared by the kernels and their
-// launchers: which rows of Q, K, V, O and LSE one (sequence, head) owns.
+// The dense and packed batch layouts shared by the kernels, their launchers
+// and the host-side validation: which rows of Q, K, V, O and LSE one
+// (sequence, head) owns.  Plain C++ (no device code), so host-only builds of
+// the validation layer can include it.
 #pragma once
-#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -20,28 +21,5 @@ struct SeqShape {
   int H, group;
   int Nq, Nk;
 };
-struct SeqSpan {
-  size_t q_row0, k_row0;  // first Q/O/LSE row and first K/V row of the (sequence, head)
-  int nq, nk;             // its query and key counts
-};
-__device__ __forceinline__ SeqSpan seq_span(const SeqShape& a, int s, int h) {
-  SeqSpan r;
-  const int hk = h / a.group;
-  if (a.cu_q != nullptr) {
-    // offsets clamped into [0, total] and made non-decreasing, so malformed
-    // offsets can only select wrong rows of this head, never memory outside it
-    const int qa = min(max(a.cu_q[s], 0), a.Nq), ka = min(max(a.cu_k[s], 0), a.Nk);
-    r.nq = min(max(a.cu_q[s + 1], qa), a.Nq) - qa;
-    r.nk = min(max(a.cu_k[s + 1], ka), a.Nk) - ka;
-    r.q_row0 = (size_t)h * a.Nq + qa;
-    r.k_row0 = (size_t)hk * a.Nk + ka;
-  } else {
-    r.nq = a.Nq;
-    r.nk = a.Nk;
-    r.q_row0 = ((size_t)s * a.H + h) * a.Nq;
-    r.k_row0 = ((size_t)s * (a.H / a.group) + hk) * a.Nk;
-  }
-  return r;
-}
 
 }  // namespace attn

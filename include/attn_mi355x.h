@@ -34,8 +34,11 @@
  *     allocates or frees device memory and keeps no mutable global state:
  *     calls are reentrant and thread-safe.  Asynchronous GPU faults surface
  *     at the caller's next synchronisation.
- *   - Every argument is validated before anything is launched.  A negative
- *     return value means nothing was launched.  There is no silent fallback
+ *   - Every argument is validated before anything is launched: a return of
+ *     ATTN_E_INVALID, ATTN_E_UNSUPPORTED or ATTN_E_WORKSPACE means nothing
+ *     was launched.  ATTN_E_HIP reports a launch error; the entry points
+ *     that run several kernels stop at the first such error, but kernels
+ *     enqueued before it in the same call may still run.  There is no silent fallback
  *     to another algorithm: an unsupported head size or dtype is an error
  *     (the silent math-path fallback criticised in "Integration in eight
  *     lines" is exactly what this library refuses to do).

@@ -26,25 +26,6 @@ from __future__ import annotations
 import numpy as np
 
 
-def causal_visible(Nq: int, Nk: int) -> np.ndarray:
-    """Boolean [Nq, Nk]: True where key j is visible to query i (bottom-right
-    aligned causal mask)."""
-    if Nq > Nk:
-        raise ValueError("causal attention needs Nq <= Nk")
-    i = np.arange(Nq)[:, None]
-    j = np.arange(Nk)[None, :]
-    return j <= i + (Nk - Nq)
-
-
-def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
-    """S = scale * Q K^T for one head ([Nq, d] x [Nk, d] -> [Nq, Nk]) in fp64,
-    with -inf at masked (future) positions."""
-    s = (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T) * float(scale)
-    if causal:
-        s = np.where(causal_visible(q.shape[0], k.shape[0]), s, -np.inf)
-    return s
-
-
 def softmax_rows(s: np.ndarray):
     """Row softmax of a score matrix: returns (P, m, l) with m the row max,
     l = sum_j exp(s_ij - m), P = exp(s - m) / l."""

@@ -1,49 +1,51 @@
-"""The tiled online-softmax recurrence, in fp64.  TEST INFRASTRUCTURE ONLY.
+"""The online-softmax recurrence, in fp64.  TEST INFRASTRUCTURE ONLY (see the
+package docstring for who may import it).
 
-``flash_forward_tiled`` takes the steps of [trading post], "The Flash
-Attention algorithm", in that section's order and notation: Q is cut into
-T_r = ceil(N/B_r) row blocks Q_i and K, V into T_c = ceil(N/B_c) column
-blocks K_j, V_j.  For each query block the state O_i = 0, m_i = -inf,
-l_i = 0 is carried across the key blocks:
+``online_forward`` evaluates attention the way a tiled kernel has to: it never
+holds a whole score row, only one block of keys at a time, and carries three
+running quantities per query row across the key blocks:
 
-    S_ij  = Q_i K_j^T * scale
-    m_ij  = rowmax(S_ij)
-    P_ij  = exp(S_ij - m_ij)
-    l_ij  = rowsum(P_ij)
-    m_new = max(m_i, m_ij)
-    l_new = exp(m_i - m_new) l_i + exp(m_ij - m_new) l_ij
-    O_i   = (l_i exp(m_i - m_new) / l_new) O_i + (exp(m_ij - m_new) / l_new) P_ij V_j
-    m_i, l_i = m_new, l_new
+  * ``top``  -- the largest visible score seen so far (-inf before any);
+  * ``mass`` -- the sum of exp(score - top) over the keys seen so far;
+  * ``acc``  -- the sum of exp(score - top) * v over the same keys.
 
-i.e. the output is renormalised after every block (the form of the first
-FlashAttention).  "The online softmax recurrence" states that the result is
-algebraically the two-pass softmax; the tests hold this function to the plain
-definition in ``oracle.attention`` at 1e-12.
+When a new block raises ``top``, the history is brought to the new reference
+by one factor exp(top_old - top_new); that is the rescaling of "The online
+softmax recurrence" in [trading post] (an accumulated output is scaled down
+as if the new maximum had been known from the start).  The division by the
+total mass is left to the very end, the deferred normalisation that the
+"FA2" section of the same post gives as its first change (fewer non-matmul
+operations in the inner loop).  Splitting Q into row blocks and K, V into key
+blocks follows "The Flash Attention algorithm"; the block sizes are free
+parameters, and "The online softmax recurrence" says the result is the
+two-pass softmax in exact arithmetic, which the tests hold this function to
+(``oracle.attention`` at 1e-12 for many block shapes).
 
-Readings where the section is silent:
-  * a tile row whose keys are all masked has m_ij = -inf; it contributes
-    nothing (P_ij = 0, l_ij = 0) instead of exp(-inf - -inf) = NaN;
-  * LSE is m + ln(l) of the final state (the stored (m, l) statistics of
-    "Backward: recompute instead of store").
+Readings where the pages are silent:
+  * a row that has not yet seen a visible key keeps top = -inf and zero mass
+    and accumulator; exp(-inf) = 0 is used for both its history factor and
+    its masked scores, so no NaN arises from -inf - -inf;
+  * LSE is top + ln(mass) of the final state: the stored softmax statistics
+    (m, l) of "Backward: recompute instead of store", folded into one number.
 
-``merge_states`` combines partial results computed over disjoint key ranges.
-It is the same update as the last two lines above, applied to states that
-are already normalised: with L_s = m_s + ln l_s, the merged state is
-L = M + ln sum_s exp(L_s - M) (M = max_s L_s) and O = sum_s exp(L_s - L) O_s.
-A state whose range saw no visible key has L_s = -inf and weight 0.
+``merge_states`` combines normalised partial results computed over disjoint
+key ranges (the split-KV decode): with L_s = ln of each part's mass plus its
+top, the merged L = M + ln sum_s exp(L_s - M) (M = max_s L_s) and
+O = sum_s exp(L_s - L) O_s, the same rescale-and-add step applied to whole
+ranges; a part that saw no visible key has L_s = -inf and weight 0.
 
 Parity status: pinned (equality with the two-pass definition for several
-block sizes and masks; split-and-merge equality with the whole-range result).
+block shapes and masks, the definition's own closed-form pins, planted
+mistakes in tests/test_oracle_mutations.py; split-and-merge equality with the
+whole-range result).
 """
 from __future__ import annotations
-
-import math
 
 import numpy as np
 
 
-def flash_forward_tiled(q, k, v, scale: float, causal: bool = False,
-                        B_r: int = 16, B_c: int = 16):
+def online_forward(q, k, v, scale: float, causal: bool = False,
+                   rows_per_block: int = 16, keys_per_block: int = 16):
     """One head, q [Nq, d], k [Nk, d], v [Nk, dv].  Returns (O, LSE) fp64."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -51,38 +53,29 @@ def flash_forward_tiled(q, k, v, scale: float, causal: bool = False,
     Nq, Nk = q.shape[0], k.shape[0]
     if causal and Nq > Nk:
         raise ValueError("causal attention needs Nq <= Nk")
-    T_r = math.ceil(Nq / B_r)
-    T_c = math.ceil(Nk / B_c)
-    O = np.zeros((Nq, v.shape[1]))
-    LSE = np.zeros(Nq)
-    for i in range(T_r):
-        rows = np.arange(i * B_r, min(Nq, (i + 1) * B_r))
-        Q_i = q[rows]
-        O_i = np.zeros((len(rows), v.shape[1]))
-        m_i = np.full(len(rows), -np.inf)
-        l_i = np.zeros(len(rows))
-        for j in range(T_c):
-            cols = np.arange(j * B_c, min(Nk, (j + 1) * B_c))
-            K_j, V_j = k[cols], v[cols]
-            S_ij = Q_i @ K_j.T * float(scale)
+    out = np.empty((Nq, v.shape[1]))
+    lse = np.empty(Nq)
+    for r0 in range(0, Nq, rows_per_block):
+        qrows = np.arange(r0, min(Nq, r0 + rows_per_block))
+        top = np.full(len(qrows), -np.inf)
+        mass = np.zeros(len(qrows))
+        acc = np.zeros((len(qrows), v.shape[1]))
+        for c0 in range(0, Nk, keys_per_block):
+            keys = np.arange(c0, min(Nk, c0 + keys_per_block))
+            block = (q[qrows] @ k[keys].T) * float(scale)
             if causal:
-                S_ij = np.where(cols[None, :] <= rows[:, None] + (Nk - Nq), S_ij, -np.inf)
-            m_ij = S_ij.max(axis=1)
-            live = np.isfinite(m_ij)
-            m_ref = np.where(live, m_ij, 0.0)
-            P_ij = np.where(live[:, None], np.exp(S_ij - m_ref[:, None]), 0.0)
-            l_ij = P_ij.sum(axis=1)
-            m_new = np.maximum(m_i, m_ij)
-            # exp(-inf - finite) = 0; rows still without any visible key keep l = 0
-            a_old = np.where(np.isfinite(m_i), np.exp(m_i - np.where(np.isfinite(m_new), m_new, 0.0)), 0.0)
-            a_new = np.where(live, np.exp(m_ij - np.where(np.isfinite(m_new), m_new, 0.0)), 0.0)
-            l_new = l_i * a_old + l_ij * a_new
-            safe = np.where(l_new > 0, l_new, 1.0)
-            O_i = O_i * (l_i * a_old / safe)[:, None] + (P_ij @ V_j) * (a_new / safe)[:, None]
-            m_i, l_i = m_new, l_new
-        O[rows] = O_i
-        LSE[rows] = m_i + np.log(l_i)
-    return O, LSE
+                future = keys[None, :] > qrows[:, None] + (Nk - Nq)
+                block = np.where(future, -np.inf, block)
+            new_top = np.maximum(top, block.max(axis=1))
+            ref = np.where(np.isfinite(new_top), new_top, 0.0)
+            history = np.exp(top - ref)
+            weights = np.exp(block - ref[:, None])
+            mass = mass * history + weights.sum(axis=1)
+            acc = acc * history[:, None] + weights @ v[keys]
+            top = new_top
+        out[qrows] = acc / mass[:, None]
+        lse[qrows] = top + np.log(mass)
+    return out, lse
 
 
 def merge_states(O_parts, LSE_parts):

@@ -161,13 +161,14 @@ def pin_rows_sum_to_one(softmax_rows, tol=1e-13):
 # ---------------------------------------------------------------- recurrence
 
 def pin_recurrence_equals_definition(tiled, definition, tol=1e-12):
-    """The tiled recurrence equals the two-pass definition (the trading post's
-    online-softmax section states they agree in exact arithmetic)."""
+    """The blocked online recurrence equals the two-pass definition (the
+    trading post's online-softmax section states they agree in exact
+    arithmetic), for block shapes from one key to more than the whole row."""
     for (Nq, Nk, d, causal, br, bc) in [(9, 13, 4, False, 4, 3), (16, 16, 8, True, 5, 7),
                                         (5, 12, 3, True, 2, 1), (20, 20, 4, True, 16, 16),
                                         (7, 30, 6, False, 7, 64), (12, 12, 2, True, 3, 4)]:
         q, k, v = _rand(Nq, d) * 2, _rand(Nk, d) * 2, _rand(Nk, 5)
-        O1, L1 = tiled(q, k, v, 0.4, causal, B_r=br, B_c=bc)
+        O1, L1 = tiled(q, k, v, 0.4, causal, rows_per_block=br, keys_per_block=bc)
         O2, L2 = definition(q, k, v, 0.4, causal)
         assert np.max(np.abs(O1 - O2)) <= tol and np.max(np.abs(L1 - L2)) <= tol
 

@@ -13,6 +13,29 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 A = 0x10000          # a fake, 16-byte aligned address: never dereferenced (validation fails first)
 MIS = 0x10008        # misaligned
 
+# tests/test_abi_sanitized.py runs this file again against a CPU build of the
+# same validation layer (api.cpp, plan.cpp) under AddressSanitizer and
+# UndefinedBehaviorSanitizer, whose kernel launchers are stubs that only count
+# launches; there the calls that pass every check run too (stub_only tests).
+VALIDATION_LIB = os.environ.get("ATTN_VALIDATION_LIB")
+if VALIDATION_LIB:
+    Bd.LIB_PATH = VALIDATION_LIB
+    Bd._lib = None
+stub_only = pytest.mark.skipif(not VALIDATION_LIB, reason="an accepted call launches kernels: checked against the "
+                                                           "stub launchers of the sanitizer build only")
+SPAN_MAX = (1 << 31) - (1 << 16)   # largest head of Q, K, V or O in bytes (buffer-resource span)
+
+
+def launches() -> int:
+    return ctypes.CDLL(Bd.LIB_PATH).attn_stub_launches()
+
+
+def accepted(call) -> bool:
+    """The call passed validation and asked for exactly one launch sequence."""
+    before = launches()
+    rc = call()
+    return rc == Bd.ATTN_OK and launches() > before
+
 
 def declared_functions():
     text = open(HEADER).read()
@@ -52,8 +75,10 @@ def fwd(**kw):
     (dict(scale=float("nan")), Bd.ATTN_E_INVALID), (dict(scale=float("inf")), Bd.ATTN_E_INVALID),
     (dict(causal=1, Nq=5, Nk=4), Bd.ATTN_E_INVALID),
     (dict(B=2 ** 20, H=2 ** 20), Bd.ATTN_E_INVALID),
-    # one head of K past 2^32 bytes (the prefill's 32-bit buffer descriptors)
+    # one head of K or Q past the buffer-resource span (2^31 - 2^16 bytes)
     (dict(Nk=2 ** 24, d=128), Bd.ATTN_E_INVALID), (dict(Nq=2 ** 25, Nk=2 ** 25, d=64), Bd.ATTN_E_INVALID),
+    (dict(Nk=SPAN_MAX // 256 + 1, d=128), Bd.ATTN_E_INVALID),
+    (dict(Nq=SPAN_MAX // 128 + 1, Nk=SPAN_MAX // 128 + 1, d=64), Bd.ATTN_E_INVALID),
     (dict(d=96), Bd.ATTN_E_UNSUPPORTED), (dict(d=256), Bd.ATTN_E_UNSUPPORTED), (dict(dtype=2), Bd.ATTN_E_UNSUPPORTED),
     (dict(Nq=1, ws=None, wsb=0), Bd.ATTN_E_WORKSPACE), (dict(Nq=1, ws=A, wsb=16), Bd.ATTN_E_WORKSPACE),
     (dict(Nq=1, ws=MIS, wsb=1 << 20), Bd.ATTN_E_WORKSPACE),
@@ -209,7 +234,8 @@ def test_gqa_and_varlen_reject():
     assert vl(cq=A + 2) == Bd.ATTN_E_INVALID
     assert vl(nseq=0) == Bd.ATTN_E_INVALID and vl(Hkv=3) == Bd.ATTN_E_INVALID
     assert vl(mq=-1) == Bd.ATTN_E_INVALID and vl(scale=0.0) == Bd.ATTN_E_INVALID
-    assert vl(mk=2 ** 25) == Bd.ATTN_E_INVALID       # one sequence's keys past 2^32 bytes
+    assert vl(mk=2 ** 25) == Bd.ATTN_E_INVALID       # one sequence's keys past the span limit
+    assert vl(mk=SPAN_MAX // 128 + 1) == Bd.ATTN_E_INVALID
     assert vl(d=96) == Bd.ATTN_E_UNSUPPORTED
     assert vl(mq=0) == Bd.ATTN_OK                      # no query: nothing launched
     bg = lambda **kw: L.attn_bwd_gqa(A, A, A, A, A, A, A, A, A, 1, kw.get("H", 8), kw.get("Hkv", 2), 16, 16, 128,
@@ -257,3 +283,43 @@ def test_exp2_split_rejects():
     assert L.attn_debug_exp2_poly(A, A, 0, None) == Bd.ATTN_E_INVALID
     assert L.attn_debug_exp2_poly(None, A, 8, None) == Bd.ATTN_E_INVALID
     assert L.attn_debug_exp2_poly(A + 2, A, 8, None) == Bd.ATTN_E_INVALID
+
+
+@stub_only
+def test_span_limit_both_sides():
+    """Heads of exactly SPAN_MAX bytes are accepted, one row more is rejected:
+    the bound the kernels' buffer resources are sized for (every offset they
+    form, a prefetched tile past the end included, stays below 2^31)."""
+    L = Bd.lib()
+    for d in (64, 128):
+        n = SPAN_MAX // (2 * d)
+        assert n * 2 * d == SPAN_MAX
+        assert accepted(lambda: fwd(Nq=8, Nk=n, d=d))
+        assert fwd(Nq=8, Nk=n + 1, d=d) == Bd.ATTN_E_INVALID
+        assert accepted(lambda: fwd(Nq=n, Nk=n, d=d, causal=1))
+        assert fwd(Nq=n + 1, Nk=n + 1, d=d) == Bd.ATTN_E_INVALID
+        assert accepted(lambda: bwd(B=1, H=1, Nq=8, Nk=n, d=d))
+        assert bwd(B=1, H=1, Nq=8, Nk=n + 1, d=d) == Bd.ATTN_E_INVALID
+        vl = lambda mk: L.attn_fwd_varlen(A, A, A, A, A, A, A, 2, 64, mk, 128, 2 * mk, 4, 2, d, 0.1, 0, 0, None)
+        assert accepted(lambda: vl(n))
+        assert vl(n + 1) == Bd.ATTN_E_INVALID
+
+
+@stub_only
+def test_valid_calls_launch():
+    """Every entry point launches once its arguments pass, and never when
+    they fail (a rejected call leaves the launch count unchanged)."""
+    L = Bd.lib()
+    assert accepted(lambda: fwd())
+    assert accepted(lambda: fwd(Nq=1, ws=A, wsb=1 << 20))
+    assert accepted(lambda: bwd())
+    assert accepted(lambda: L.attn_fwd_gqa(A, A, A, A, A, 1, 8, 2, 16, 16, 128, 0.1, 1, 0, None, 0, None))
+    assert accepted(lambda: L.attn_fwd_q8(A, A, A, A, A, A, A, None, 1, 2, 8, 8, 128, 0.1, 0, None))
+    assert accepted(lambda: L.attn_quantize_tensor_e4m3(A, A, A, 1 << 20, A, 1 << 20, None))
+    assert accepted(lambda: L.attn_rotate_quantize_e4m3(A, A, A, A, 2, 64, 128, 64, None))
+    assert accepted(lambda: L.attn_fwd_exp2_split(A, A, A, A, A, 1, 1, 8, 8, 128, 0.1, 0, 0, 2, None))
+    before = launches()
+    assert fwd(d=96) == Bd.ATTN_E_UNSUPPORTED and bwd(ws=None) == Bd.ATTN_E_WORKSPACE
+    assert L.attn_fwd_q8(A, A, A, None, A, A, A, None, 1, 2, 8, 8, 128, 0.1, 0, None) == Bd.ATTN_E_INVALID
+    assert launches() == before
+

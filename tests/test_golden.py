@@ -25,7 +25,8 @@ def test_attention_closed_forms(case):
     O_exp = np.array([[_ev(x) for x in row] for row in case["O"]])
     L_exp = np.array([_ev(x) for x in case["LSE"]])
     for fn in (lambda: A.attention_head(q, k, v, case["scale"], case["causal"]),
-               lambda: R.flash_forward_tiled(q, k, v, case["scale"], case["causal"], B_r=1, B_c=2)):
+               lambda: R.online_forward(q, k, v, case["scale"], case["causal"], rows_per_block=1,
+                                        keys_per_block=2)):
         O, L = fn()
         assert np.max(np.abs(O - O_exp)) <= 1e-14
         assert np.max(np.abs(L - L_exp)) <= 1e-14

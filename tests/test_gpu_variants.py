@@ -203,3 +203,31 @@ def test_varlen_backward(F, dtype, d, causal, case):
     _, L = V.attention_varlen(f(q), f(k), f(v), cq, ck, wq.scale, causal)
     assert np.all(got[0][~np.isfinite(L)] == 0.0)
     _check_grads(got, ref)
+
+
+def test_varlen_backward_without_queries(F):
+    """A packed batch whose sequences hold keys but no query at all
+    (total_q = 0, total_k > 0): the backward returns 0 and writes dK = dV = 0.
+    The query-side tensors are empty, so the call goes through the C ABI with
+    small stand-in buffers for them (the library reads no query row)."""
+    import ctypes
+    import torch
+    from flashattention_forward_amd import binding as Bd
+    H, Hkv, d = 2, 1, 64
+    ck = torch.tensor([0, 5, 135], dtype=torch.int32, device="cuda")
+    cq = torch.zeros(3, dtype=torch.int32, device="cuda")
+    g = torch.Generator().manual_seed(11)
+    k = torch.randn(Hkv, 135, d, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(Hkv, 135, d, generator=g).to(torch.bfloat16).cuda()
+    dk, dv = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    stand_in = torch.zeros(64, device="cuda", dtype=torch.bfloat16)
+    lse_in = torch.zeros(16, device="cuda", dtype=torch.float32)
+    ws = torch.zeros(64, device="cuda", dtype=torch.uint8)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    print("  gpu: varlen bwd, 2 sequences, keys (5, 130), no queries", flush=True)
+    rc = Bd.lib().attn_bwd_varlen(p(stand_in), p(k), p(v), p(stand_in), p(stand_in), p(lse_in), p(stand_in), p(dk),
+                                  p(dv), p(cq), p(ck), 2, 0, 130, 0, 135, H, Hkv, d, 0.125, 0, Bd.ATTN_BF16, p(ws),
+                                  64, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert rc == Bd.ATTN_OK, Bd.status_str(rc)
+    assert bool((dk == 0).all()) and bool((dv == 0).all())

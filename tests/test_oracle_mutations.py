@@ -75,48 +75,39 @@ def test_attention_mistake_is_caught(mistake):
     assert failed, f"no pin catches {mistake}"
 
 
-def tiled_variant(q, k, v, scale, causal, B_r=3, B_c=2, mistake=None):
+def tiled_variant(q, k, v, scale, causal, rows_per_block=3, keys_per_block=2, mistake=None):
     """The recurrence of oracle.recurrence with one switchable mistake."""
     q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
     Nq, Nk = q.shape[0], k.shape[0]
-    O = np.zeros((Nq, v.shape[1]))
-    LSE = np.zeros(Nq)
-    for i in range(math.ceil(Nq / B_r)):
-        rows = np.arange(i * B_r, min(Nq, (i + 1) * B_r))
-        O_i = np.zeros((len(rows), v.shape[1]))
-        m_i = np.full(len(rows), -np.inf)
-        l_i = np.zeros(len(rows))
-        for j in range(math.ceil(Nk / B_c)):
-            cols = np.arange(j * B_c, min(Nk, (j + 1) * B_c))
-            S = q[rows] @ k[cols].T * scale
+    out = np.empty((Nq, v.shape[1]))
+    lse = np.empty(Nq)
+    for r0 in range(0, Nq, rows_per_block):
+        qrows = np.arange(r0, min(Nq, r0 + rows_per_block))
+        top = np.full(len(qrows), -np.inf)
+        mass = np.zeros(len(qrows))
+        acc = np.zeros((len(qrows), v.shape[1]))
+        for c0 in range(0, Nk, keys_per_block):
+            keys = np.arange(c0, min(Nk, c0 + keys_per_block))
+            block = (q[qrows] @ k[keys].T) * float(scale)
             if causal:
-                S = np.where(cols[None, :] <= rows[:, None] + (Nk - Nq), S, -np.inf)
-            m_ij = S.max(axis=1)
-            live = np.isfinite(m_ij)
-            Pm = np.where(live[:, None], np.exp(S - np.where(live, m_ij, 0.0)[:, None]), 0.0)
-            l_ij = Pm.sum(axis=1)
-            m_new = np.maximum(m_i, m_ij)
-            mref = np.where(np.isfinite(m_new), m_new, 0.0)
-            a_old = np.where(np.isfinite(m_i), np.exp(m_i - mref), 0.0)
-            a_new = np.where(live, np.exp(m_ij - mref), 0.0)
-            if mistake == "old_state_not_rescaled":
-                a_old = np.where(np.isfinite(m_i), 1.0, 0.0)
-            if mistake == "new_block_not_rescaled":
-                a_new = live.astype(float)
-            l_new = l_i * a_old + l_ij * a_new
-            safe = np.where(l_new > 0, l_new, 1.0)
-            if mistake == "output_not_renormalised":
-                O_i = O_i * a_old[:, None] + (Pm @ v[cols]) * (a_new / safe)[:, None]
-            else:
-                O_i = O_i * (l_i * a_old / safe)[:, None] + (Pm @ v[cols]) * (a_new / safe)[:, None]
-            m_i = m_ij if mistake == "max_not_running" else m_new
-            l_i = l_new
-        O[rows] = O_i
-        LSE[rows] = m_i + np.log(l_i)
-    return O, LSE
+                block = np.where(keys[None, :] > qrows[:, None] + (Nk - Nq), -np.inf, block)
+            bmax = block.max(axis=1)
+            new_top = np.maximum(top, bmax)
+            ref = np.where(np.isfinite(new_top), new_top, 0.0)
+            history = np.exp(top - ref)
+            if mistake == "history_not_rescaled":
+                history = np.where(np.isfinite(top), 1.0, 0.0)
+            wref = np.where(np.isfinite(bmax), bmax, 0.0) if mistake == "block_own_max" else ref
+            weights = np.exp(block - wref[:, None])
+            mass = (mass if mistake == "mass_not_rescaled" else mass * history) + weights.sum(axis=1)
+            acc = acc * history[:, None] + weights @ v[keys]
+            top = bmax if mistake == "max_not_running" else new_top
+        out[qrows] = acc if mistake == "no_final_division" else acc / mass[:, None]
+        lse[qrows] = top + np.log(mass)
+    return out, lse
 
 
-TILED_MISTAKES = ["old_state_not_rescaled", "new_block_not_rescaled", "output_not_renormalised",
+TILED_MISTAKES = ["history_not_rescaled", "mass_not_rescaled", "block_own_max", "no_final_division",
                   "max_not_running"]
 
 
@@ -125,7 +116,7 @@ def test_unmutated_tiled_copy_equals_oracle():
     q, k, v = rng.standard_normal((7, 4)), rng.standard_normal((11, 4)), rng.standard_normal((11, 3))
     for causal in (False, True):
         o1, l1 = tiled_variant(q, k, v, 0.5, causal)
-        o2, l2 = R.flash_forward_tiled(q, k, v, 0.5, causal, B_r=3, B_c=2)
+        o2, l2 = R.online_forward(q, k, v, 0.5, causal, rows_per_block=3, keys_per_block=2)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 

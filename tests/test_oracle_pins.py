@@ -13,7 +13,7 @@ def _definition(q, k, v, scale, causal):
 
 
 def _tiled(q, k, v, scale, causal):
-    return R.flash_forward_tiled(q, k, v, scale, causal, B_r=3, B_c=2)
+    return R.online_forward(q, k, v, scale, causal, rows_per_block=3, keys_per_block=2)
 
 
 @pytest.mark.parametrize("pin", P.ATTENTION_PINS, ids=lambda f: f.__name__)
@@ -55,7 +55,7 @@ def test_softmax_rows_pin():
 
 
 def test_recurrence_equals_definition():
-    P.pin_recurrence_equals_definition(R.flash_forward_tiled,
+    P.pin_recurrence_equals_definition(R.online_forward,
                                        lambda q, k, v, s, c: A.attention_head(q, k, v, s, c))
 
 
