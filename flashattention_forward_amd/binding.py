@@ -28,6 +28,7 @@ SIGNATURES = {
     "attn_fwd_decode_splits": (_I, [_I, _I, _I, _I]),
     "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "attn_fwd_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "attn_fwd_decode_static": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
     "attn_bwd_gqa": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),

@@ -111,6 +111,19 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* out, floa
   return decode_impl(q, k, v, out, lse, B, H, H, Nk, d, scale, dtype, num_splits, workspace, workspace_bytes, stream);
 }
 
+int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nk,
+                           int d, float scale, int dtype, int num_splits, void* stream) {
+  int rc = check_common(q, k, v, out, lse, B, H, 1, Nk, scale, 0);
+  if (rc != ATTN_OK) return rc;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_E_UNSUPPORTED;
+  if (num_splits < 1 || num_splits > 256 || num_splits > Nk) return ATTN_E_INVALID;
+  if (!decode_sizes_ok(B, H, num_splits)) return ATTN_E_INVALID;
+  if (attn::decode_workspace_bytes(B, H, d, num_splits) > attn::kDecodeStaticScratchBytes) return ATTN_E_WORKSPACE;
+  return hip_status(attn::launch_decode_static(q, k, v, out, lse, B, H, Nk, d, scale, dtype == ATTN_BF16,
+                                               num_splits, static_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq, int Nk, int d,
              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, out, lse, B, H, H, Nq, Nk, d, scale, causal, dtype, workspace, workspace_bytes, stream);
@@ -353,7 +366,8 @@ const char* attn_status_str(int status) {
     case ATTN_OK: return "ok";
     case ATTN_E_INVALID: return "invalid argument (null/misaligned pointer, bad or too large size, bad scale, causal with Nq > Nk)";
     case ATTN_E_UNSUPPORTED: return "unsupported head size or dtype";
-    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_WORKSPACE:
+      return "workspace missing or too small (attn_fwd_decode_static: partials larger than its static scratch)";
     case ATTN_E_HIP: return "HIP launch error";
     default: return "unknown status";
   }

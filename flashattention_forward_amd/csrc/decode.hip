@@ -19,6 +19,7 @@
 // A second kernel merges the ranges: LSE = M + ln sum_s exp(LSE_s - M),
 // O = sum_s exp(LSE_s - LSE) O_s -- the same running-statistics update
 // applied to states over disjoint key ranges.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -446,6 +447,50 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
   if (d == 64 && !bf16)
     return launch_decode_g<64, false>(q, k, v, out, lse, B, H, Hkv, Nk, scale, splits, workspace, stream);
   return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------- decode without allocation
+// Split partials of attn_fwd_decode_static, for callers that cannot allocate
+// device memory (code under graph capture, serving loops, harnesses that
+// forbid allocation): a file-scope device array that every GPU the library
+// runs on holds from module load to process end.  Host code must not pass
+// the array's own name to a kernel (on the host it is only a stand-in, not a
+// device address): its device address is looked up once per device with
+// hipGetSymbolAddress and used from then on.  The partial kernels write every
+// (head, split) slot that the merge kernel reads, so nothing in it has to be
+// cleared between calls; two calls that overlap on one GPU share it and race.
+static __device__ __align__(256) unsigned char scratch[kDecodeStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device id
+}  // namespace
+
+hipError_t decode_static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_static(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                                int Nk, int d, float scale, bool bf16, int splits, hipStream_t stream) {
+  if (decode_workspace_bytes(B, H, d, splits) > kDecodeStaticScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = decode_static_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_decode(q, k, v, out, lse, B, H, H, Nk, d, scale, bf16, splits, ws, stream);
 }
 
 }  // namespace attn

@@ -40,6 +40,13 @@ int decode_default_splits(int B, int H, int Hkv, int Nk, int d);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* out, float* lse,
                          int B, int H, int Hkv, int Nk, int d, float scale, bool bf16, int splits,
                          void* workspace, hipStream_t stream);
+// The same decode with its split partials in the library's static device
+// scratch (no workspace argument, no allocation); needs
+// decode_workspace_bytes(B, H, d, splits) <= kDecodeStaticScratchBytes.
+constexpr size_t kDecodeStaticScratchBytes = (size_t)8 << 20;
+hipError_t launch_decode_static(const void* q, const void* k, const void* v, void* out, float* lse,
+                                int B, int H, int Nk, int d, float scale, bool bf16, int splits,
+                                hipStream_t stream);
 
 // Backward pass: preprocess (log-sum-exp in base 2, rowsum(dO * O)) into a
 // float2 workspace with one entry per query row (q_rows of them: B*H*Nq dense,

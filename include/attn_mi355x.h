@@ -158,6 +158,25 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* out, floa
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same split-KV decode with the same arguments minus the workspace.  The
+ * split partials (B*H*num_splits*(d+1) floats, attn_decode_workspace_bytes())
+ * go to a static device array of ATTN_DECODE_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; this call
+ * allocates and frees nothing.  Larger partials are refused with
+ * ATTN_E_WORKSPACE before anything is launched.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller; calls in order
+ * on one stream are safe, and nothing in the array needs clearing between
+ * them.  The first call on a device looks the array's address up once.
+ */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES (8u << 20)
+int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int H, int Nk, int d, float scale, int dtype, int num_splits,
+                           void* stream);
+
+/*
  * Attention backward: the gradients of sum(dout * out) with respect to q, k
  * and v, for out = attention(q, k, v) as computed by attn_fwd (same scale and
  * causal flag).  The probability tiles are rebuilt from q, k and the

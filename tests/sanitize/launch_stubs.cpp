@@ -28,6 +28,10 @@ hipError_t launch_decode(const void*, const void*, const void*, void*, float*, i
                          int, void*, hipStream_t) {
   return launched();
 }
+hipError_t launch_decode_static(const void*, const void*, const void*, void*, float*, int, int, int, int, float, bool,
+                                int, hipStream_t) {
+  return launched();
+}
 hipError_t launch_bwd(const void*, const void*, const void*, const void*, const void*, const float*, void*, void*,
                       void*, const SeqShape&, int, int, int, long, int, float, bool, bool, void*, hipStream_t) {
   return launched();

@@ -323,3 +323,29 @@ def test_valid_calls_launch():
     assert L.attn_fwd_q8(A, A, A, None, A, A, A, None, 1, 2, 8, 8, 128, 0.1, 0, None) == Bd.ATTN_E_INVALID
     assert launches() == before
 
+
+def test_static_decode_rejects():
+    """attn_fwd_decode_static: attn_fwd_decode's checks, and partials larger
+    than the static scratch (8 MiB) refused before any launch."""
+    L = Bd.lib()
+    st = lambda B=2, H=2, Nk=64, d=128, ns=4, dt=0, q=A: L.attn_fwd_decode_static(q, A, A, A, A, B, H, Nk, d, 0.1,
+                                                                                   dt, ns, None)
+    assert st(ns=0) == Bd.ATTN_E_INVALID and st(ns=65) == Bd.ATTN_E_INVALID and st(q=None) == Bd.ATTN_E_INVALID
+    assert st(d=80) == Bd.ATTN_E_UNSUPPORTED and st(dt=7) == Bd.ATTN_E_UNSUPPORTED
+    assert 64 * 32 * 16 * 129 * 4 > 8 << 20
+    assert st(B=64, H=32, Nk=4096, ns=16) == Bd.ATTN_E_WORKSPACE
+
+
+@stub_only
+def test_static_decode_scratch_limit_both_sides():
+    """Partials of exactly 8 MiB fit the static scratch; one split more does not."""
+    L = Bd.lib()
+    # B*H*splits*(d+1)*4 bytes: 16*32*16*(127+1)... with d = 128: 129 floats per (head, split)
+    B, H, d = 1, 1, 128
+    fit = (8 << 20) // ((d + 1) * 4)            # (head, split) slots that fit
+    H = 254                                       # 254 heads x splits slots
+    s = fit // H                                  # largest split count that fits
+    assert H * s * (d + 1) * 4 <= 8 << 20 < H * (s + 1) * (d + 1) * 4
+    call = lambda ns: L.attn_fwd_decode_static(A, A, A, A, A, B, H, 1 << 16, d, 0.1, 0, ns, None)
+    assert accepted(lambda: call(s))
+    assert call(s + 1) == Bd.ATTN_E_WORKSPACE
