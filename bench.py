@@ -265,6 +265,131 @@ def cpu_baseline(seconds_target: float = 15.0, max_heads: int = 1024):
                       f"fp64 numpy, {dt:.1f} s incl. input generation"}
 
 
+def cpu_oracle_other(seconds_each: float = 4.0):
+    """The fp64 oracle beside the other workloads, each on a bounded sample
+    timed on this host: the long causal sequence (query rows of one head
+    against all their visible keys), the decode (whole (batch, head) pairs,
+    GB/s over their K and V bytes) and the quantised forward (query rows of
+    one head, int8 scores and E4M3 P as the oracle emulates them; the head's
+    quantisation is outside the timed part)."""
+    import numpy as np
+    import fa_inputs as G
+    from oracle import attention as A
+    from oracle import quant as Q
+    out = {}
+    # long causal sequence: rows spread over the head, each against its visible keys
+    w = G.WORKLOADS["long_23400_causal"]
+    q, k, v = (G.to_f64(x[0], "fp16") for x in G.draw_qkv(w, heads=[(0, 0)]))
+    flops, rows_done, t0 = 0.0, 0, time.perf_counter()
+    # blocks of 64 rows at a stride of 2339 across the head, each pass shifted
+    # by 64 rows, until the time budget is spent
+    for i in range(w.Nq):
+        r0 = (i * 2339 + (i // 10) * 64) % (w.Nq - 63)
+        rows = np.arange(r0, r0 + 64)
+        A.attention_rows(q, k, v, rows, w.scale, True)
+        flops += float(np.sum(4.0 * w.d * (rows + 1)))
+        rows_done += len(rows)
+        if time.perf_counter() - t0 > seconds_each:
+            break
+    dt = time.perf_counter() - t0
+    out["long_23400_causal"] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                                "sample": f"{rows_done} query rows of one head (fp16, causal), {dt:.1f} s"}
+    # decode: whole (batch, head) pairs
+    w = G.WORKLOADS["decode_8k"]
+    heads = [divmod(i, w.H) for i in range(32)]
+    drawn = [tuple(G.to_f64(x[0], "bf16") for x in G.draw_qkv(w, heads=[bh])) for bh in heads]
+    nbytes, pairs, t0 = 0.0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds_each:
+        q, k, v = drawn[pairs % len(drawn)]
+        A.attention_head(q, k, v, w.scale, False)
+        nbytes += 2.0 * w.Nk * w.d * 2
+        pairs += 1
+    dt = time.perf_counter() - t0
+    out["decode_8k"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s",
+                        "sample": f"{pairs} (batch, head) decodes over 32 drawn pairs, inputs drawn beforehand, "
+                                  f"{dt:.1f} s"}
+    # quantised forward: query rows of one head
+    w = G.WORKLOADS["quant_8k"]
+    q, k, v = (G.to_f32(x[0], "bf16") for x in G.draw_qkv(w, heads=[(0, 0)]))
+    qi = Q.quantize_inputs(q, k, v)
+    ops, rows_done, t0 = 0.0, 0, time.perf_counter()
+    for r0 in range(0, w.Nq, 512):
+        rows = slice(r0, r0 + 128)
+        Q.attention_q8_head(qi["q8"][rows], qi["sq"][rows], qi["k8"], qi["sk"], qi["v8"], qi["sv"], w.scale)
+        ops += 4.0 * w.d * w.Nk * 128
+        rows_done += 128
+        if time.perf_counter() - t0 > seconds_each:
+            break
+    dt = time.perf_counter() - t0
+    out["quant_8k"] = {"value": round(ops / dt / 1e12, 6), "unit": "TOP/s",
+                       "sample": f"{rows_done} query rows of one head (int8 scores, E4M3 P), {dt:.1f} s"}
+    return out
+
+
+def rescale_stats(heads: int = 4):
+    """How often the running max is raised (O and l rescaled), emulated on the
+    CPU over the bench inputs, per (wave of 32 query rows, key tile) pair, for
+    three rules: raise on every increase of a row's max (the plain online
+    softmax), raise only when a tile's max exceeds the running max by more
+    than 8 in log2 units (a threshold on the max), and this library's rule
+    (raise when a lane's probabilities against the current max would sum past
+    2^14; a lane holds the keys 4h..4h+3 of every 8 of the tile).  A wave
+    raises when any of its rows (lanes) does.  The first visible tile of a
+    row always sets its max and is counted apart."""
+    import numpy as np
+    import fa_inputs as G
+    log2e = 1.4426950408889634
+    out = {}
+    cases = [("prefill_4k", G.WORKLOADS["prefill_4k"], "bf16", 64), ("prefill_4k_causal",
+             G.WORKLOADS["prefill_4k_causal"], "bf16", 64), ("long_23400_causal", G.WORKLOADS["long_23400_causal"],
+                                                              "fp16", 128)]
+    for name, w, dt, BN in cases:
+        cnt = {"every_increase": 0, "max_plus_8": 0, "tile_sum_2^14": 0, "first_tiles": 0, "wave_tiles": 0}
+        for hd in range(heads):
+            b, h = divmod(hd * 7 % (w.B * w.H), w.H)
+            q, k = (G.to_f64(x[0], dt) for x in G.draw_qkv(w, heads=[(b, h)])[:2])
+            Nq, Nk = q.shape[0], k.shape[0]
+            for r0 in range(0, Nq, 32):
+                rows = np.arange(r0, min(Nq, r0 + 32))
+                s = (q[rows] @ k.T) * (w.scale * log2e)
+                if w.causal:
+                    s = np.where(np.arange(Nk)[None, :] <= rows[:, None] + (Nk - Nq), s, -np.inf)
+                    kv_end = min(Nk, (r0 // 256 + 1) * 256 + (Nk - Nq))   # the workgroup's last visible key
+                else:
+                    kv_end = Nk
+                m0 = np.full(len(rows), -np.inf)
+                m8 = m0.copy()
+                ms = m0.copy()
+                half = (np.arange(BN) % 8) >= 4
+                for t0 in range(0, kv_end, BN):
+                    T = s[:, t0:t0 + BN]
+                    tm = T.max(axis=1)
+                    cnt["wave_tiles"] += 1
+                    if np.all(np.isneginf(ms)) and np.any(np.isfinite(tm)):
+                        cnt["first_tiles"] += 1
+                    if np.any(tm > m0) and not np.all(np.isneginf(m0)):
+                        cnt["every_increase"] += 1
+                    m0 = np.maximum(m0, tm)
+                    if np.any(tm > m8 + 8) and not np.all(np.isneginf(m8)):
+                        cnt["max_plus_8"] += 1
+                    m8 = np.where(tm > m8 + 8, np.maximum(m8, tm), m8)
+                    if np.any(np.isneginf(ms)):
+                        ms = np.maximum(ms, tm)
+                    else:
+                        with np.errstate(over="ignore"):
+                            p = np.exp2(T - ms[:, None])
+                        hs = np.stack([p[:, ~half[:T.shape[1]]].sum(axis=1), p[:, half[:T.shape[1]]].sum(axis=1)])
+                        if np.any(~(hs <= 2.0 ** 14)):
+                            cnt["tile_sum_2^14"] += 1
+                            ms = np.maximum(ms, tm)
+        n = cnt["wave_tiles"]
+        out[name] = {**cnt, "heads": heads, "tile_keys": BN,
+                     "rate_every_increase": round(cnt["every_increase"] / n, 5),
+                     "rate_max_plus_8": round(cnt["max_plus_8"] / n, 5),
+                     "rate_tile_sum": round(cnt["tile_sum_2^14"] / n, 5)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,7 +403,13 @@ def main():
     ap.add_argument("--decode-traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--quant-only", action="store_true")
+    ap.add_argument("--long-only", action="store_true", help="the long causal sequence alone (counter runs)")
+    ap.add_argument("--rescale-stats", action="store_true",
+                    help="CPU only: how often each max-raising rule rescales, on the bench inputs")
     args = ap.parse_args()
+    if args.rescale_stats:
+        print(json.dumps(rescale_stats()))
+        return
     if args.traffic_from:
         print(json.dumps(traffic_from(*args.traffic_from)))
         return
@@ -313,6 +444,16 @@ def main():
         _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, scale=wd.scale, out=o, lse=l, workspace=ws)],
                                 args.steps, args.warmup)
         print(json.dumps({"workload": "decode_8k", "ms": round(per[0] * 1e3, 4)}))
+        return
+    if args.long_only:
+        # the long causal fp16 sequence alone (for its counter runs)
+        wl = G.WORKLOADS["long_23400_causal"]
+        tq, tk, tv = (G.to_torch(x, "fp16") for x in G.draw_qkv(wl, threads=16))
+        o = torch.empty_like(tq)
+        l = torch.empty((wl.B, wl.H, wl.Nq), device="cuda")
+        _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, causal=True, scale=wl.scale, out=o, lse=l)],
+                                args.steps, args.warmup)
+        print(json.dumps({"workload": "long_23400_causal", "ms": round(per[0] * 1e3, 4)}))
         return
     if args.quant_only:
         # the quantised forward of quant_8k alone (int8 scores, E4M3 P.V; for its counter runs)
@@ -549,8 +690,11 @@ def main():
         torch.cuda.empty_cache()
         res["other_workloads"] = other
 
+    res["build_info"] = F.build_info()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
+        if not args.no_extra:
+            res["cpu_oracle_other"] = cpu_oracle_other()
     print(json.dumps(res), flush=True)
 
 

@@ -69,6 +69,10 @@ struct PrefillCfg {
   static constexpr int MB_O = D / 32;        // 32-row blocks of O^T
   static constexpr int NA = NB * KSTEPS;     // MFMAs of S^T per tile
   static constexpr int NC = NG * MB_O;       // MFMAs of O^T per tile
+  // half of P(t) formed inside the GEMM phase (d = 64, where the softmax is the
+  // longer phase: twice the scores per MFMA of d = 128); at d = 128 the GEMM
+  // phase is the longer one and the softmax stays whole in its own phase
+  static constexpr bool EARLY = D == 64;
   static_assert(NA == NC, "S and PV MFMA streams are interleaved one to one");
   static_assert(NA % NLD == 0, "loads are spread evenly over the MFMA steps");
 };
@@ -90,8 +94,9 @@ __device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 
 // exponent field.  The cubic is our relative-error minimax fit of 2^f on
 // [0, 1] (Remez exchange; flashattention_forward_amd/exp2_poly_fit.py
 // reproduces these fp32 coefficients); its relative error is at most 7.5e-5,
-// and arguments below -125 (masked keys, -inf) give 0; from -125 up every
-// result is a normal fp32 number, so adding n to the exponent field is exact.
+// and arguments below -125 (masked keys, -inf) give 0; from -125 up to 128
+// every result is a normal fp32 number, so adding n to the exponent field is
+// exact; arguments from 128 up give +inf (the softmax's overflow check sees it).
 constexpr float kExp2C0 = 0.9999251961708069f, kExp2C1 = 0.6958335638046265f, kExp2C2 = 0.22606715559959412f,
                 kExp2C3 = 0.07802452147006989f;
 __device__ __forceinline__ float exp2_poly(float x) {
@@ -100,12 +105,15 @@ __device__ __forceinline__ float exp2_poly(float x) {
   const float f = xc - n;
   const float p = fmaf(fmaf(fmaf(kExp2C3, f, kExp2C2), f, kExp2C1), f, kExp2C0);
   const float r = __builtin_bit_cast(float, __builtin_bit_cast(int, p) + ((int)n << 23));
-  return x < -125.f ? 0.f : r;
+  return x < -125.f ? 0.f : (x >= 128.f ? INFINITY : r);
 }
 
-// Raise the running max only when a tile exceeds it by more than this
-// (log2 units): P = exp2(s - m) then stays below 2^8.
-constexpr float kRescaleThreshold = 8.0f;
+// Largest sum of one lane's probabilities in a tile, P = exp2(s c - m), before
+// the running max m is raised: every P then stays at or below 2^14, inside the
+// range of the fp16 P operand (largest finite 65504) and far inside that of
+// bf16 and of the fp32 O and l accumulators; the result after the final
+// division by l does not depend on m.
+constexpr float kMaxTileSum = 16384.0f;
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -215,8 +223,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
       va_off[mb] = vrow * C::ROWB + 16 * ((col >> 3) ^ v_swz<D>(vrow)) + 2 * (col & 7);
     }
-    auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i%NB, k-step i/NB
-      return lds_load<op8>(lk, ka_off[i / C::NB] + (i % C::NB) * 32 * C::ROWB);
+    auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i/KSTEPS, k-step i%KSTEPS
+      return lds_load<op8>(lk, ka_off[i % C::KSTEPS] + (i / C::KSTEPS) * 32 * C::ROWB);
     };
     auto va_load = [&](const char* lv, int j) {  // V^T operand of O^T step j: 16-key group j/MB_O, d block j%MB_O
       const uint32_t a0 = va_off[j % C::MB_O] + 16 * (j / C::MB_O) * C::ROWB;
@@ -251,14 +259,56 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       op8 pb[C::NG];    // P(t) between its softmax phase and the next GEMM phase
       float m_run = -INFINITY, l_run = 0.f;
 
+      // P of one half of the key blocks of S(t) against the reference m_ref: half 0
+      // is S blocks [0, NB/2) -> P groups [0, NG/2), half 1 the rest.  Writes those
+      // P groups and returns this lane's sum of the P it formed.
+      auto exps_half = [&](int half, float m_ref) {
+        float lsum[4];
+#pragma unroll
+        for (int gg = 0; gg < C::NG / 2; ++gg) {
+          const int g = half * (C::NG / 2) + gg;
+          const int nb = g >> 1, tt = g & 1;
+          op2 pr[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x0 = fmaf(s[nb][8 * tt + 2 * j], c, -m_ref);
+            const float x1 = fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_ref);
+            const float p0 = 2 * j < SWX ? exp2_poly(x0) : __builtin_amdgcn_exp2f(x0);
+            const float p1 = 2 * j + 1 < SWX ? exp2_poly(x1) : __builtin_amdgcn_exp2f(x1);
+            pr[j] = M::pack2(p0, p1);
+            lsum[j] = gg == 0 ? p0 + p1 : lsum[j] + (p0 + p1);
+          }
+          pb[g] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                          __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+      };
+      // tile t holds keys a row of this wave must not see (causal diagonal, or keys
+      // past Nk): wave-uniform
+      auto edge_tile = [&](int t) {
+        const int kv0 = t * C::BN;
+        return (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
+      };
+      float lsum_a = 0.f;  // this lane's sum over the first half of P(t), formed during G_t
+
       // ---- G_t: S(t) (t < T) and O += P(t-1) V(t-1) (t >= 1), MFMA streams interleaved;
       // lk holds K(t), lv holds V(t-1).  With LD (group 0) it also issues the loads
       // of K(t+1) into ldk and V(t) into ldv, one every STEP MFMA steps, so that the
       // address unit sees a steady trickle rather than every wave's loads at once.
       // K(t+1) is loaded even when t+1 = T: those rows read as 0 or are never used.
+      // S(t) is formed key block by key block and P(t-1) is consumed group by group,
+      // so after half the steps the first half of S(t) is final and the first half
+      // of the P operand registers is free.  With EARLY the first half of P(t) is
+      // then formed against the running max, its vector instructions interleaved
+      // with the remaining MFMAs (the softmax phase takes it over, or forms it
+      // again, when the tile is masked, has no running max yet, or overflows the
+      // bound).
       auto gemm_phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool LD, int t, const char* lk, const char* lv,
                             char* ldk, char* ldv) {
         constexpr int STEP = C::NA / C::NLD;
+        // vector instructions of the half softmax per remaining MFMA step (about 27
+        // per 16-key group: 8 FMA, 8 exp2, 7 adds, 4 conversions)
+        constexpr int kValuPerStep = (27 * (C::NG / 2) + C::NA / 2 - 1) / (C::NA / 2);
         const bool do_s = t < T, do_pv = t >= 1;
         if (do_s && do_pv) {
 #pragma unroll
@@ -270,6 +320,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             ka[i] = ka_load(lk, i);
             va[i] = va_load(lv, i);
           }
+          const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+          (void)m_ref;
 #pragma unroll
           for (int i = 0; i < C::NA; ++i) {
             const op8 a = ka[i % PF], b = va[i % PF];
@@ -277,12 +329,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
               ka[i % PF] = ka_load(lk, i + PF);
               va[i % PF] = va_load(lv, i + PF);
             }
-            s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
+            s[i / C::KSTEPS] = M::mma(a, qop[i % C::KSTEPS], s[i / C::KSTEPS]);
             o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
             if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
+            if (C::EARLY && i == C::NA / 2 - 1) lsum_a = exps_half(0, m_ref);
           }
           // issue order: the first PF steps' operand reads, then per step its two
-          // MFMAs each followed by the reads of the step PF ahead, then its load
+          // MFMAs each followed by the reads of the step PF ahead, then its load;
+          // in the second half of the steps the half softmax fills the gaps
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * PF, 0);
 #pragma unroll
           for (int i = 0; i < C::NA; ++i) {
@@ -291,6 +345,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
             if (LD && i % STEP == STEP - 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            if (C::EARLY && i >= C::NA / 2) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerStep, 0);
           }
         } else if (do_s) {
 #pragma unroll
@@ -302,7 +357,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
           for (int i = 0; i < C::NA; ++i) {
             const op8 a = ka[i & 1];
             if (i + 2 < C::NA) ka[i & 1] = ka_load(lk, i + 2);
-            s[i % C::NB] = M::mma(a, qop[i / C::NB], s[i % C::NB]);
+            s[i / C::KSTEPS] = M::mma(a, qop[i % C::KSTEPS], s[i / C::KSTEPS]);
             if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
           }
         } else if (do_pv) {
@@ -321,53 +376,63 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       // ---- X_t: mask, running max, rescale, P(t) = exp2(S c - m), row sum
       auto softmax_phase = [&](int t) {
         const int kv0 = t * C::BN;
-        if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
-          const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
+        const bool edge = edge_tile(t);
+        if (edge) {
+          // element i of block nb holds key kv0 + 4h + e with e = 32 nb + 8 (i/4) + i%4;
+          // it is visible iff e <= lim.  The select is a bit blend with the all-ones
+          // or all-zeros word (lim - e) >> 31, so no per-element compare results
+          // have to be held in scalar registers.
+          const int lim = min(Nk - 1, CAUSAL ? qrow + off : Nk - 1) - (kv0 + 4 * h);
+          constexpr uint32_t kNegInf = 0xFF800000u;
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int key = kv0 + 32 * nb + 8 * (i >> 2) + 4 * h + (i & 3);
-              if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
+              const int e = 32 * nb + 8 * (i >> 2) + (i & 3);
+              const uint32_t hide = (uint32_t)((lim - e) >> 31);
+              // the element is copied out first: a bit cast applied to a vector
+              // element lvalue in place read element 0 of the vector here
+              const float v = s[nb][i];
+              const uint32_t bits = __builtin_bit_cast(uint32_t, v);
+              s[nb][i] = __builtin_bit_cast(float, (bits & ~hide) | (kNegInf & hide));
             }
         }
-        float mx[C::NB];
+        // P(t) against the running max as it stands.  The tile's own row max is
+        // only formed when that fails: on a row's first tile (no max yet), or when
+        // a lane's probabilities would sum past kMaxTileSum.  Then the running max
+        // is raised to the row max, O and l are rescaled, and P(t) is formed again.
+        bool raise = __any(m_run == -INFINITY);
+        // the first half of P(t) formed during G_t stands unless the tile was masked
+        // here afterwards, G_t had no P(t-1) to consume (t = 0), or the max is raised
+        const bool have_a = C::EARLY && t >= 1 && !edge && !raise;
+        float tot;
+        for (;;) {
+          if (raise) {
+            float mx[C::NB];
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          mx[nb] = fmaxf(s[nb][0], s[nb][1]);
+            for (int nb = 0; nb < C::NB; ++nb) {
+              mx[nb] = fmaxf(s[nb][0], s[nb][1]);
 #pragma unroll
-          for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
-        }
+              for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
+            }
 #pragma unroll
-        for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
-        const float mt = pair_max(mx[0]) * c;
-        float alpha = 1.f;
-        if (__any(mt > m_run + kRescaleThreshold)) {
-          const float m_new = fmaxf(m_run, mt);
-          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
+            const float m_new = fmaxf(m_run, pair_max(mx[0]) * c);
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-          for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
-          m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int g = 0; g < C::NG; ++g) {
-          const int nb = g >> 1, tt = g & 1;
-          op2 pr[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x0 = fmaf(s[nb][8 * tt + 2 * j], c, -m_use);
-            const float x1 = fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_use);
-            const float p0 = 2 * j < SWX ? exp2_poly(x0) : __builtin_amdgcn_exp2f(x0);
-            const float p1 = 2 * j + 1 < SWX ? exp2_poly(x1) : __builtin_amdgcn_exp2f(x1);
-            pr[j] = M::pack2(p0, p1);
-            lsum[j] += p0 + p1;
+            for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
           }
-          pb[g] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                          __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+          // a row that has seen no visible key keeps m = -inf: exponent base 0, P = 0
+          const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+          const float a = (have_a && !raise) ? lsum_a : exps_half(0, m_use);
+          tot = a + exps_half(1, m_use);
+          // not (tot <= bound) also catches an overflow to inf
+          if (raise || !__any(!(tot <= kMaxTileSum))) break;
+          raise = true;
         }
-        l_run = fmaf(l_run, alpha, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+        l_run += tot;
       };
 
       // prologue: K(0) into LDS

@@ -4,9 +4,11 @@ exp2_poly), checked on the CPU against the mathematics.
 * Its fp32 coefficients are those of the Remez fit.
 * The fit equioscillates within 7.5e-5 relative error on [0, 1].
 * The kernel's evaluation steps, emulated in fp32, stay within that bound
-  (plus fp32 rounding) of the exact 2^x over the arguments the softmax
-  produces: -125 .. 8 in log2 units, integers and their neighbours included.
-  Arguments below -125, and -inf (masked keys), give 0.
+  (plus fp32 rounding) of the exact 2^x from -125 up to 128 (the softmax
+  accepts tiles whose probabilities stay at or below 2^14; larger arguments
+  only have to be large enough for its overflow check), integers and their
+  neighbours included.  Arguments below -125, and -inf (masked keys), give
+  0; arguments from 128 up give +inf.
 A planted sign error in the range reduction breaks the bound."""
 import os
 import re
@@ -41,18 +43,18 @@ def emulate(x, c=None, flip=False):
     f = (n - xc if flip else xc - n).astype(np.float32)
     k = lambda v: np.full(f.shape, v, np.float32)
     p = _fma32(_fma32(_fma32(k(c[3]), f, k(c[2])), f, k(c[1])), f, k(c[0]))
-    r = (p.view(np.int32) + (n.astype(np.int32) << 23)).view(np.float32)
-    return np.where(x < -125.0, np.float32(0.0), r)
+    r = (p.view(np.int32) + (np.minimum(n, 127).astype(np.int32) << 23)).view(np.float32)
+    return np.where(x < -125.0, np.float32(0.0), np.where(x >= 128.0, np.float32(np.inf), r))
 
 
 def grid():
     rng = np.random.default_rng(7)
-    ints = np.arange(-125, 9, dtype=np.float32)
+    ints = np.arange(-125, 128, dtype=np.float32)
     near = np.concatenate([np.nextafter(ints, np.float32(-np.inf)), np.nextafter(ints, np.float32(np.inf))])
-    dense = np.linspace(-125.0, 8.0, 1_000_001, dtype=np.float32)
-    rand = rng.uniform(-125.0, 8.0, 500_000).astype(np.float32)
-    x = np.concatenate([ints, near, dense, rand])
-    return x[(x >= -125.0) & (x <= 8.0)]
+    dense = np.linspace(-125.0, 16.0, 1_000_001, dtype=np.float32)
+    rand = rng.uniform(-125.0, 128.0, 500_000).astype(np.float32)
+    x = np.concatenate([ints, near, dense, rand, [np.nextafter(np.float32(128.0), np.float32(0.0))]])
+    return x[(x >= -125.0) & (x < 128.0)]
 
 
 def rel_err(y, x):
@@ -89,6 +91,11 @@ def test_underflow_and_masked_keys_give_zero():
     assert np.all(emulate(x) == 0.0)
     # 2^-125 itself is kept
     assert abs(float(emulate(np.array([-125.0], np.float32))[0]) / 2.0 ** -125 - 1.0) <= BOUND
+
+
+def test_overflow_gives_inf():
+    x = np.array([128.0, 128.5, 300.0, 1e30, np.inf], np.float32)
+    assert np.all(np.isposinf(emulate(x)))
 
 
 def test_planted_sign_error_is_caught():

@@ -39,6 +39,8 @@ def test_exp2_poly_within_bound(F):
     assert rel_err(y, x).max() <= BOUND
     z = np.array([-125.5, -126.0, -300.0, -np.inf], np.float32)
     assert np.all(F.debug_exp2_poly(torch.from_numpy(z).cuda()).cpu().numpy() == 0.0)
+    big = np.array([128.0, 200.0, np.inf], np.float32)
+    assert np.all(np.isposinf(F.debug_exp2_poly(torch.from_numpy(big).cuda()).cpu().numpy()))
 
 
 def _run_split(F, w, causal, poly, seed=0):
