@@ -25,12 +25,15 @@
 //   * Softmax in the exp2 domain: p = exp2(s * scale * log2(e) - m), one FMA
 //     and one v_exp_f32 per score; the row sum l adds the fp32 P (rounding P
 //     to bf16 first would cost up to 2^-8 of l on rows with few keys).
-//   * The running max is only raised when a tile's max exceeds it by more
-//     than 8 in log2 units (the adaptive rescaling of "Smarter online softmax
-//     rescaling" in the linux-konsole.com post "FlashAttention 4: fast,
-//     memory-efficient attention for LLMs"): P then stays below 2^8, and O
-//     and l are rescaled only on those rare tiles.  The result is exact
-//     after the final 1/l.
+//   * The running max is raised only when P would otherwise grow too large
+//     (the adaptive rescaling of "Smarter online softmax rescaling" in the
+//     linux-konsole.com post "FlashAttention 4: fast, memory-efficient
+//     attention for LLMs"): P(t) is formed against the running max as it
+//     stands, and only on a row's first tile, or when a lane's P over the
+//     tile sums past 2^14, is the max raised, O and l rescaled and P(t)
+//     formed again.  P stays at or below 2^14 (inside fp16), no tile max is
+//     formed on the common path, and the result after the final 1/l does
+//     not depend on where m stands.
 //   * Two groups of 4 waves alternate: while one group runs the MFMAs of its
 //     tile (S(t) and O += P(t-1) V(t-1), the two streams interleaved), the
 //     other runs the softmax of its previous tile, so the matrix cores and
@@ -401,36 +404,39 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         // only formed when that fails: on a row's first tile (no max yet), or when
         // a lane's probabilities would sum past kMaxTileSum.  Then the running max
         // is raised to the row max, O and l are rescaled, and P(t) is formed again.
-        bool raise = __any(m_run == -INFINITY);
+        const bool first = __any(m_run == -INFINITY);
         // the first half of P(t) formed during G_t stands unless the tile was masked
         // here afterwards, G_t had no P(t-1) to consume (t = 0), or the max is raised
-        const bool have_a = C::EARLY && t >= 1 && !edge && !raise;
-        float tot;
-        for (;;) {
-          if (raise) {
-            float mx[C::NB];
+        const bool have_a = C::EARLY && t >= 1 && !edge && !first;
+        float tot = 0.f;
+        bool raise = first;
+        if (!first) {
+          const float a = have_a ? lsum_a : exps_half(0, m_run);
+          tot = a + exps_half(1, m_run);
+          // not (tot <= bound) also catches an overflow to inf
+          raise = __any(!(tot <= kMaxTileSum));
+        }
+        // the row max is formed only here, on the rare raising tiles (a loop around
+        // both paths let the compiler hoist it onto every tile)
+        if (raise) {
+          float mx[C::NB];
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
-              mx[nb] = fmaxf(s[nb][0], s[nb][1]);
+          for (int nb = 0; nb < C::NB; ++nb) {
+            mx[nb] = fmaxf(s[nb][0], s[nb][1]);
 #pragma unroll
-              for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
-            }
-#pragma unroll
-            for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
-            const float m_new = fmaxf(m_run, pair_max(mx[0]) * c);
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
-            l_run *= alpha;
-            m_run = m_new;
+            for (int i = 2; i < 16; ++i) mx[nb] = fmaxf(mx[nb], s[nb][i]);
           }
+#pragma unroll
+          for (int nb = 1; nb < C::NB; ++nb) mx[0] = fmaxf(mx[0], mx[nb]);
+          const float m_new = fmaxf(m_run, pair_max(mx[0]) * c);
+          const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+          for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
           // a row that has seen no visible key keeps m = -inf: exponent base 0, P = 0
           const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-          const float a = (have_a && !raise) ? lsum_a : exps_half(0, m_use);
-          tot = a + exps_half(1, m_use);
-          // not (tot <= bound) also catches an overflow to inf
-          if (raise || !__any(!(tot <= kMaxTileSum))) break;
-          raise = true;
+          tot = exps_half(0, m_use) + exps_half(1, m_use);
         }
         l_run += tot;
       };
