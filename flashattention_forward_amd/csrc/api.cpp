@@ -379,7 +379,8 @@ const char* attn_build_info(void) {
          "direct-to-LDS K/V tiles, 32x32x16 MFMA, S^T=KQ^T, V^T via ds_read_b64_tr_b16, running max raised only when "
          "a lane's tile P sums past 2^14, causal blocks paired on large grids; "
          "decode split-KV 256 threads, 8 rows in flight/lane + LSE merge (static 8 MiB scratch variant); "
-         "q8 prefill d=128 BM=128 BN=64, int8 32x32x32 + fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8; "
+         "q8 prefill d=128 BM=128 BN=64 (3 workgroups/CU, double-buffered direct-to-LDS K8/V8 tiles), int8 32x32x32 + "
+         "fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8; "
          "backward: (lse, D) preprocess, dK/dV kernel (128 keys/WG, 32-query steps, K and V rows resident), "
          "dQ kernel (128 queries/WG, 32-key steps), no atomics";
 }

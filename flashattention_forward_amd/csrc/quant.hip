@@ -12,10 +12,15 @@
 //   * P^T is converted to E4M3 in registers (v_cvt_pk_fp8_f32, round to
 //     nearest even) and fed to v_mfma_f32_32x32x64_f8f6f4 as the B operand:
 //     a lane's 32 values of a 64-key tile are exactly one k-step;
-//   * the V8 tile is written to LDS with its rows permuted so that the 32
-//     keys each half-wave holds in the S^T accumulator are 32 consecutive
-//     LDS rows; four transposing 8-bit LDS reads (ds_read_b64_tr_b8) then
-//     give every lane its 32 V values in the same key order;
+//   * K8 (with its key scales) and V8 tiles go from global memory straight
+//     into double-buffered LDS, rows permuted so that the 32 keys each
+//     half-wave holds in the S^T accumulator are 32 consecutive LDS rows;
+//     four transposing 8-bit LDS reads (ds_read_b64_tr_b8) then give every
+//     lane its 32 V values in the same key order;
+//   * the softmax is vector-ALU bound (its exponentials, conversions and
+//     scales outweigh the 8-bit MFMAs), so each wave runs its tile's matrix
+//     and vector work in turn and three workgroups per CU (three waves per
+//     SIMD) interleave them;
 //   * l sums the fp32 P (only the MFMA operand is quantised) and the epilogue
 //     applies v_scale / l.
 // The quantisation kernels (per-token int8, per-tensor E4M3) and two test
@@ -315,16 +320,15 @@ __global__ __launch_bounds__(256) void rotate_quantize_e4m3_kernel(const uint16_
 
 // ------------------------------------------------------------ quantised tiles
 struct Q8Cfg {
-  static constexpr int D = 128, BM = 128, BN = 64, NT = 256;
-  static constexpr int KSTRIDE = D + 16;   // LDS bytes per K8 row
-  static constexpr int VSTRIDE = D + 32;   // LDS bytes per (permuted) V8 row
-  static constexpr int KBYTES = BN * KSTRIDE;
-  static constexpr int VBYTES = BN * VSTRIDE;
-  static constexpr int CPR = D / 16;       // 16-byte chunks per row
-  static constexpr int RPP = NT / CPR;     // rows per staging pass (32)
-  static constexpr int PASSES = BN / RPP;  // 2
-  static constexpr int KSTEPS = D / 32;    // int8 MFMA k-steps
-  static constexpr int MB_O = D / 32;
+  static constexpr int D = 128, BM = 128, BN = 64, NT = 256;  // 4 waves of 32 query rows
+  static constexpr int ROWB = D;                 // bytes per K8 / V8 row
+  static constexpr int SPR = ROWB / 16;          // 16-byte slots per row
+  static constexpr int TILEB = BN * ROWB;        // bytes per K8 or V8 tile
+  static constexpr int KBUF = TILEB + BN * 4;    // K8 tile followed by its 64 key scales
+  static constexpr int RPI = 1024 / ROWB;        // rows per 1 KB wave load
+  static constexpr int LPW = TILEB / 1024 / 4;   // 1 KB loads per K8 or V8 tile for each wave
+  static constexpr int KSTEPS = D / 32;          // int8 k-steps per 32-key block
+  static constexpr int MB_O = D / 32;            // 32-row blocks of O^T
 };
 
 // Key order of a score tile.  The K8 tile is staged so that row 8g + 4h + r
@@ -334,100 +338,71 @@ struct Q8Cfg {
 // byte (or nibble) j of lane half h is key 32h + j, which is the V row the
 // transposing V^T read of that half returns at position j, so V rows are
 // staged in key order.
-__device__ __forceinline__ int k8_lds_row(int kt) {
-  const int h = kt >> 5, nb = (kt >> 4) & 1, g = (kt >> 2) & 3, r = kt & 3;
-  return 32 * nb + 8 * g + 4 * h + r;
-}
-__device__ __forceinline__ int score_key(int nb, int i, int h) { return 32 * h + 16 * nb + i; }
-
 // The mixed fp8 x fp4 MFMA pairs its operands by K index, and the two
 // formats lay K out differently: fp4 element j of lane half h is K = 32h + j
 // (the P nibbles, key 32h + j as above), fp8 element j of lane half h is
 // K = 16h + j for j < 16 and 32 + 16h + (j - 16) for j >= 16.  For P in fp4
 // the V row of tile key kt is therefore staged at the LDS row whose
 // transposed read lands on the fp8 element with K index kt.
-__device__ __forceinline__ int v8_lds_row_p4(int kt) {
-  return kt < 32 ? 32 * (kt >> 4) + (kt & 15) : 32 * ((kt - 32) >> 4) + 16 + (kt & 15);
+__device__ __forceinline__ int score_key(int nb, int i, int h) { return 32 * h + 16 * nb + i; }
+
+// tile key held by LDS row R of a K8 tile: row 8g + 4h + r of score block nb
+// holds key 32h + 16nb + 4g + r
+__device__ __forceinline__ int k8_row_key(int R) {
+  return 32 * ((R >> 2) & 1) + 16 * (R >> 5) + 4 * ((R >> 3) & 3) + (R & 3);
+}
+// tile key held by LDS row R of a V8 tile: R itself, or for FP4 P the key
+// whose fp8 K index the transposed read of row R lands on
+template <bool P4>
+__device__ __forceinline__ int v8_row_key(int R) {
+  if (!P4) return R;
+  return ((R >> 4) & 1) ? 32 + 16 * (R >> 5) + (R & 15) : 16 * (R >> 5) + (R & 15);
+}
+// slot swizzles: the K operand reads (16 lanes read one slot of 16 consecutive
+// rows) and the transposing V reads (16 lanes read 16 bytes of 8 consecutive
+// rows) then hit distinct banks
+__device__ __forceinline__ int k8_swz(int R) { return (R >> 1) & 7; }
+__device__ __forceinline__ int v8_swz(int R) { return (R >> 1) & 3; }
+
+// direct global -> LDS loads: lane i's BYTES bytes at voff land at dst + BYTES i
+__device__ __forceinline__ void q8_load_lds16(const __amdgpu_buffer_rsrc_t& r, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void q8_load_lds4(const __amdgpu_buffer_rsrc_t& r, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)dst, 4, voff, 0, 0, 0);
 }
 
-// B operand of S^T = K8 Q8^T: lane holds Q8[qrow][32kk + 16h .. +15].
-__device__ __forceinline__ void load_q8_operand(const int8_t* Q8row, bool valid, int h, i32x4* qop) {
-#pragma unroll
-  for (int kk = 0; kk < Q8Cfg::KSTEPS; ++kk) {
-    i32x4 x = {0, 0, 0, 0};
-    if (valid) x = reinterpret_cast<const i32x4*>(Q8row)[2 * kk + h];
-    qop[kk] = x;
-  }
-}
-
-// Exact int32 S^T for the 64 keys of the K8 tile in LDS and the lane's query:
-// acc[nb][i] = sum_t K8[LDS row 32nb + 8(i/4) + 4h + i%4][t] * Q8[q][t], i.e.
-// the score of tile key score_key(nb, i, h).
-__device__ __forceinline__ void qk_tile_i8(const char* lk, const i32x4* qop, int l32, int h, i32x16* acc) {
+// S^T of one 64-key K8 tile held in LDS against the lane's query: acc[nb][i]
+// is the score of tile key score_key(nb, i, h), exact int32 (F8 false; |S| <=
+// 127^2 d < 2^24) or fp32 from E4M3 codes (F8 true: each fp8 step contracts
+// 64 of d, its operands two int8-form 32-wide chunks side by side, A and B
+// paired byte for byte).  ka_off[kk]: the lane's byte offset of int8 k-step kk
+// in key block 0; qop[kk]: Q8[qrow][32kk + 16h .. +15].
+template <bool F8>
+__device__ __forceinline__ void qk_tile(const char* lk, const i32x4* qop, const uint32_t* ka_off,
+                                        typename std::conditional<F8, f32x16, i32x16>::type* acc) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    acc[nb] = i32x16{};
+    acc[nb] = {};
+    if constexpr (F8) {
 #pragma unroll
-    for (int kk = 0; kk < Q8Cfg::KSTEPS; ++kk) {
-      const i32x4 a = lds_load<i32x4>(lk, (32 * nb + l32) * Q8Cfg::KSTRIDE + 32 * kk + 16 * h);
-      acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[kk], acc[nb], 0, 0, 0);
-    }
-  }
-}
-
-// fp32 S^T for the 64 keys of the E4M3 K8 tile in LDS and the lane's E4M3
-// query: each fp8 step contracts 64 of d, its operands being two int8-form
-// 32-wide chunks side by side (A and B paired byte for byte, so every d is
-// matched with itself); products are exact, sums fp32.
-__device__ __forceinline__ void qk_tile_f8(const char* lk, const i32x4* qop, int l32, int h, f32x16* acc) {
+      for (int j = 0; j < Q8Cfg::KSTEPS / 2; ++j) {
+        const i32x4 a0 = lds_load<i32x4>(lk, ka_off[2 * j] + nb * 32 * Q8Cfg::ROWB);
+        const i32x4 a1 = lds_load<i32x4>(lk, ka_off[2 * j + 1] + nb * 32 * Q8Cfg::ROWB);
+        const i32x4 b0 = qop[2 * j], b1 = qop[2 * j + 1];
+        const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[nb], 0, 0, 0, 127, 0, 127);
+      }
+    } else {
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    acc[nb] = f32x16{};
-#pragma unroll
-    for (int j = 0; j < Q8Cfg::KSTEPS / 2; ++j) {
-      const int rowoff = (32 * nb + l32) * Q8Cfg::KSTRIDE + 64 * j + 16 * h;
-      const i32x4 a0 = lds_load<i32x4>(lk, rowoff);
-      const i32x4 a1 = lds_load<i32x4>(lk, rowoff + 32);
-      const i32x4 b0 = qop[2 * j], b1 = qop[2 * j + 1];
-      const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[nb], 0, 0, 0, 127, 0, 127);
-    }
-  }
-}
-
-// Stage rows [kv0, kv0 + 64) of K8 (and optionally V8) into registers; rows
-// at or beyond Nk read as zero.
-struct Q8Stage {
-  u32x4 k[Q8Cfg::PASSES], v[Q8Cfg::PASSES];
-  float ks;
-  __device__ __forceinline__ void load(const int8_t* K8, const uint8_t* V8, const float* KS, int kv0, int Nk, int tid,
-                                       bool with_v) {
-#pragma unroll
-    for (int p = 0; p < Q8Cfg::PASSES; ++p) {
-      const int row = p * Q8Cfg::RPP + tid / Q8Cfg::CPR, ch = tid % Q8Cfg::CPR;
-      const int key = kv0 + row;
-      k[p] = u32x4{0u, 0u, 0u, 0u};
-      v[p] = u32x4{0u, 0u, 0u, 0u};
-      if (key < Nk) {
-        k[p] = reinterpret_cast<const u32x4*>(K8 + (size_t)key * Q8Cfg::D)[ch];
-        if (with_v) v[p] = reinterpret_cast<const u32x4*>(V8 + (size_t)key * Q8Cfg::D)[ch];
+      for (int kk = 0; kk < Q8Cfg::KSTEPS; ++kk) {
+        const i32x4 a = lds_load<i32x4>(lk, ka_off[kk] + nb * 32 * Q8Cfg::ROWB);
+        acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[kk], acc[nb], 0, 0, 0);
       }
     }
-    ks = 0.f;
-    if (KS != nullptr && tid < Q8Cfg::BN && kv0 + tid < Nk) ks = KS[kv0 + tid];
   }
-  template <bool P4 = false>
-  __device__ __forceinline__ void store(char* lk, char* lv, float* lks, int tid, bool with_v) const {
-#pragma unroll
-    for (int p = 0; p < Q8Cfg::PASSES; ++p) {
-      const int row = p * Q8Cfg::RPP + tid / Q8Cfg::CPR, ch = tid % Q8Cfg::CPR;
-      lds_store<u32x4>(lk, k8_lds_row(row) * Q8Cfg::KSTRIDE + ch * 16, k[p]);
-      if (with_v) lds_store<u32x4>(lv, (P4 ? v8_lds_row_p4(row) : row) * Q8Cfg::VSTRIDE + ch * 16, v[p]);
-    }
-    if (lks != nullptr && tid < Q8Cfg::BN) lks[tid] = ks;
-  }
-};
+}
 
 // rint(127 p) of four probabilities p in [0, 1] as bytes (P's scale is the
 // constant 1/127 in the all-INT8 variant)
@@ -439,7 +414,7 @@ __device__ __forceinline__ uint32_t p_u8x4(float a, float b, float c, float d) {
 
 // VAR (QVariant): kInt8Scores -- int8 scores, E4M3 P . V; kAllInt8 -- I8V
 // below; kFp8 -- E4M3 Q8/K8 and the scores on the fp8 MFMA, P . V as in
-// kInt8Scores.
+// kInt8Scores; kFp8P4 -- kFp8 with P in MXFP4.
 // Every variant raises the running max on every increase (no lazy
 // threshold), so P = exp2(s - m_running) <= 1 when it is quantised and the
 // row's largest probability is cast as exactly 1; a lazy threshold would cast
@@ -451,183 +426,224 @@ __device__ __forceinline__ uint32_t p_u8x4(float a, float b, float c, float d) {
 // the E4M3 form's (same key order), and the exact int32 tile product is
 // added into the fp32 accumulator (a float rescale of an int32 running sum
 // would not be exact).
+// The forward: 4 waves of 32 query rows per workgroup, three workgroups per
+// CU.  Tile t+1 (K8 rows and scales, V8 rows) is requested at the start of
+// tile t into the other LDS buffer, one barrier per tile.  Each wave runs
+// S(t), the softmax and O += P(t) V(t) in turn; the workgroups' waves on a
+// SIMD interleave their matrix and vector work.
 template <bool CAUSAL, int VAR>
-__global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
+__global__ __launch_bounds__(256, 3) void prefill_q8_kernel(
     const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, float c, int nqb, int total) {
   using C = Q8Cfg;
+  constexpr int BM = C::BM, LPW = C::LPW;
   constexpr bool I8V = VAR == (int)QVariant::kAllInt8;
   constexpr bool P4 = VAR == (int)QVariant::kFp8P4;
   constexpr bool F8QK = VAR == (int)QVariant::kFp8 || P4;
-  __shared__ __attribute__((aligned(16))) char smem[C::KBYTES + C::VBYTES];
-  __shared__ __attribute__((aligned(16))) float lks[C::BN];
-  char* lk = smem;
-  char* lv = smem + C::KBYTES;
+  using SAcc = typename std::conditional<F8QK, f32x16, i32x16>::type;
+  __shared__ __attribute__((aligned(1024))) char k0s[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
 
   const int logical = xcd_remap(blockIdx.x, total);
   const int bh = logical / nqb;
   int qb = logical - bh * nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;
-  const int q0 = qb * C::BM;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest blocks first
+  const int q0 = qb * BM;
   const int off = Nk - Nq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const size_t qbase = (size_t)bh * Nq, kbase = (size_t)bh * Nk;
-  const int8_t* Kh = K8 + kbase * C::D;
-  const uint8_t* Vh = V8 + kbase * C::D;
-  const float* KSh = KS + kbase;
+  const auto rk = make_rsrc(K8 + kbase * C::D, (uint32_t)Nk * C::D);
+  const auto rv = make_rsrc(V8 + kbase * C::D, (uint32_t)Nk * C::D);
+  const auto rs = make_rsrc(KS + kbase, (uint32_t)Nk * 4);
 
-  const int qrow = q0 + 32 * w + l32;
+  // wave w fills 1 KB blocks LPW w .. LPW w + LPW-1 of each tile: lane i lands
+  // at LDS row R = block RPI + i / SPR, slot i % SPR, so it fetches the row's
+  // key and the chunk that slot holds under the swizzle
+  uint32_t gk_off[LPW], gv_off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int R = (LPW * w + i) * C::RPI + lane / C::SPR, slot = lane % C::SPR;
+    gk_off[i] = (uint32_t)k8_row_key(R) * C::ROWB + 16 * (slot ^ k8_swz(R));
+    gv_off[i] = (uint32_t)v8_row_key<P4>(R) * C::ROWB + 16 * (slot ^ v8_swz(R));
+  }
+  // tile t: K8 rows and scales into ldk, V8 rows into ldv (keys past Nk read as 0)
+  auto issue_tile = [&](int t, char* ldk, char* ldv) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      q8_load_lds16(rk, ldk + 1024 * (LPW * w + i), (uint32_t)t * C::TILEB + gk_off[i]);
+      q8_load_lds16(rv, ldv + 1024 * (LPW * w + i), (uint32_t)t * C::TILEB + gv_off[i]);
+    }
+    if (w == 0) q8_load_lds4(rs, ldk + C::TILEB, (uint32_t)(t * C::BN + lane) * 4);
+  };
+  // K operand: row l32 (+32 per key block), logical slot 2kk + h
+  uint32_t ka_off[C::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) ka_off[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ k8_swz(l32));
+  // V^T operand of d block mb: read r (0..3) covers rows 32h + 8r + r16/2,
+  // bytes 32mb + 16g1 + 8(r16&1) .. +7 of the unswizzled row
+  const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+  auto vt_load = [&](const char* lv, int mb) {
+    i32x8 a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int R = 32 * h + 8 * r + (r16 >> 1);
+      const uint32_t addr = R * C::ROWB + 16 * ((2 * mb + g1) ^ v8_swz(R)) + 8 * (r16 & 1);
+      const i32x2 x = lds_read_tr8(lv, addr);
+      a[2 * r] = x[0];
+      a[2 * r + 1] = x[1];
+    }
+    return a;
+  };
+
+  const int qmin_w = q0 + 32 * w;
+  const int qrow = qmin_w + l32;
   i32x4 qop[C::KSTEPS];
-  load_q8_operand(Q8 + (qbase + qrow) * C::D, qrow < Nq, h, qop);
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    i32x4 x = {0, 0, 0, 0};
+    if (qrow < Nq) x = reinterpret_cast<const i32x4*>(Q8 + (qbase + qrow) * C::D)[2 * kk + h];
+    qop[kk] = x;
+  }
   // query scale x softmax scale x log2 e, applied in the exponent's FMA; kept
-  // positive (a zero query row has zero scores, so its scale is immaterial) so
-  // that masked -inf scores stay -inf
+  // positive (a zero query row has zero scores) so masked -inf scores stay -inf
   const float cq = fmaxf((qrow < Nq ? QS[qbase + qrow] : 0.f) * c, FLT_MIN);
 
   int kv_end = Nk;
-  if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
-  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+  if (CAUSAL) kv_end = min(Nk, min(q0 + BM, Nq) - 1 + off + 1);
+  const int T = max(0, (kv_end + C::BN - 1) / C::BN);
 
   f32x16 o[C::MB_O];
 #pragma unroll
   for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int qmin_w = q0 + 32 * w;
 
-  Q8Stage st;
-  st.load(Kh, Vh, KSh, 0, Nk, tid, true);
-  st.store<P4>(lk, lv, lks, tid, true);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) st.load(Kh, Vh, KSh, (t + 1) * C::BN, Nk, tid, true);
+  auto tile = [&](int t, const char* lk, const char* lv, char* ldk, char* ldv) {
+    if (t + 1 < T) issue_tile(t + 1, ldk, ldv);
     const int kv0 = t * C::BN;
-    const bool skip = CAUSAL && (kv0 > qmin_w + 31 + off);
-    if (!skip) {
-      f32x16 s[2];
-      if constexpr (F8QK) {
-        qk_tile_f8(lk, qop, l32, h, s);
-      } else {
-        i32x16 acc[2];
-        qk_tile_i8(lk, qop, l32, h, acc);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[nb][i] = (float)acc[nb][i];
-      }
+    if (CAUSAL && kv0 > qmin_w + 31 + off) return;  // no key of the tile is visible to this wave
+    // S(t), scaled per key: s[nb][i] belongs to tile key 32h + 16nb + i
+    f32x16 s[2];
+    {
+      SAcc acc[2];
+      qk_tile<F8QK>(lk, qop, ka_off, acc);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 ks4 = lds_load<f32x4>(reinterpret_cast<const char*>(lks), score_key(nb, 4 * g, h) * 4);
+          const f32x4 ks4 = lds_load<f32x4>(lk, C::TILEB + (32 * h + 16 * nb + 4 * g) * 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[nb][4 * g + j] *= ks4[j];
+          for (int j = 0; j < 4; ++j) s[nb][4 * g + j] = (float)acc[nb][4 * g + j] * ks4[j];
         }
-      const bool need_mask = (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
-      if (need_mask) {
-        const int qlim = CAUSAL ? (qrow + off) : 0x7fffffff;
+    }
+    if ((kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off)) {
+      // keys past Nk or past the causal diagonal: -inf, as a bit blend (see prefill.hip)
+      const int lim = min(Nk - 1, CAUSAL ? qrow + off : Nk - 1) - (kv0 + 32 * h);
+      constexpr uint32_t kNegInf = 0xFF800000u;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + score_key(nb, i, h);
-            if (key >= Nk || key > qlim) s[nb][i] = -INFINITY;
-          }
-      }
-      float mt = s[0][0];
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t hide = (uint32_t)((lim - (16 * nb + i)) >> 31);
+          const float v = s[nb][i];
+          const uint32_t bits = __builtin_bit_cast(uint32_t, v);
+          s[nb][i] = __builtin_bit_cast(float, (bits & ~hide) | (kNegInf & hide));
+        }
+    }
+    float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+    for (int i = 2; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
-      const float mloc = mt;  // max over this lane's 32 keys (one MX block)
-      mt = pair_max(mt) * cq;
-      if (__any(mt > m_run)) {
-        const float mn = fmaxf(m_run, mt);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+    const float mloc = mt;  // max over this lane's 32 keys (one MX block)
+    mt = pair_max(mt) * cq;
+    if (__any(mt > m_run)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
-        for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
-        l_run *= alpha;
-        m_run = mn;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      // P^T as 32 E4M3 bytes (or 32 E2M1 nibbles): element j <-> s[j / 16][j % 16]
-      // MXFP4: this lane's 32 keys share 2^e, e = floor(max log2 P) - 2, so the
-      // largest P / 2^e lies in [4, 8) (E8M0 byte e + 127 for the MFMA)
-      int e_mx = -127;
-      float inv_mx = 0.f;
-      if constexpr (P4) {
-        // the rounded product, as the running max was formed from it: the
-        // block holding the row's max then has tmax == 0 exactly (a fused
-        // multiply-add would leave the product's rounding residual, and a
-        // residual just below 0 would take e one binade too low); contraction
-        // is switched off so the compiler cannot fuse it back
-        float tmax;
-        {
+      for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+      l_run *= alpha;
+      m_run = mn;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // MXFP4: the lane's 32 keys share 2^e, e = floor(max log2 P) - 2, so the
+    // largest P / 2^e lies in [4, 8) (E8M0 byte e + 127 for the MFMA).  The
+    // block max is the same rounded product the running max came from, with
+    // contraction off (a fused multiply-add's residual just below 0 would take
+    // e one binade too low)
+    int e_mx = -127;
+    float inv_mx = 0.f;
+    if constexpr (P4) {
+      float tmax;
+      {
 #pragma clang fp contract(off)
-          tmax = mloc * cq - m_use;
-        }
-        if (tmax != -INFINITY) e_mx = max(-127, (int)floorf(tmax) - 2);
-        inv_mx = __builtin_bit_cast(float, (uint32_t)(127 - e_mx) << 23);  // 2^-e, exact
+        tmax = mloc * cq - m_use;
       }
-      i32x8 pb;
+      if (tmax != -INFINITY) e_mx = max(-127, (int)floorf(tmax) - 2);
+      inv_mx = __builtin_bit_cast(float, (uint32_t)(127 - e_mx) << 23);
+    }
+    i32x8 pb;
+    float lsum = 0.f;
 #pragma unroll
-      for (int jw = 0; jw < 8; ++jw) {
-        const int nb = jw >> 2, i0 = 4 * (jw & 3);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 0], cq, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 1], cq, -m_use));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 2], cq, -m_use));
-        const float p3 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 3], cq, -m_use));
-        l_run += (p0 + p1) + (p2 + p3);
-        if constexpr (P4) {
-          // nibbles 4jw .. 4jw+3: dword jw / 2, bytes 2 (jw % 2) and 2 (jw % 2) + 1
-          const uint32_t prev = (jw & 1) ? (uint32_t)pb[jw >> 1] : 0u;
-          uint32_t w = e2m1x2_into(prev, p0 * inv_mx, p1 * inv_mx, 2 * (jw & 1));
-          w = e2m1x2_into(w, p2 * inv_mx, p3 * inv_mx, 2 * (jw & 1) + 1);
-          pb[jw >> 1] = (int)w;
-        } else {
-          pb[jw] = I8V ? (int)p_u8x4(p0, p1, p2, p3) : (int)e4m3x4(p0, p1, p2, p3);
-        }
-      }
+    for (int jw = 0; jw < 8; ++jw) {
+      const int nb = jw >> 2, i0 = 4 * (jw & 3);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 0], cq, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 1], cq, -m_use));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 2], cq, -m_use));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(s[nb][i0 + 3], cq, -m_use));
+      lsum += (p0 + p1) + (p2 + p3);
       if constexpr (P4) {
-#pragma unroll
-        for (int k = 4; k < 8; ++k) pb[k] = 0;
-      }
-      // O^T += V^T P^T: lane (h, d) reads LDS rows 32h .. 32h+31 at column d
-      const int r16 = lane & 15, g1 = (lane >> 4) & 1;
-#pragma unroll
-      for (int mb = 0; mb < C::MB_O; ++mb) {
-        i32x8 a;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t addr = (32 * h + 8 * r + (r16 >> 1)) * C::VSTRIDE + 32 * mb + 16 * g1 + 8 * (r16 & 1);
-          const i32x2 x = lds_read_tr8(lv, addr);
-          a[2 * r] = x[0];
-          a[2 * r + 1] = x[1];
-        }
-        if constexpr (I8V) {
-          i32x16 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[0], a[1], a[2], a[3]},
-                                                             i32x4{pb[0], pb[1], pb[2], pb[3]}, i32x16{}, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[4], a[5], a[6], a[7]}, i32x4{pb[4], pb[5], pb[6], pb[7]},
-                                                      acc, 0, 0, 0);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) o[mb][j] += (float)acc[j];  // |acc| < 64 * 127^2 < 2^24: exact
-        } else if constexpr (P4) {
-          o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 4, 0, 127, 0, e_mx + 127);
-        } else {
-          o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 0, 0, 127, 0, 127);
-        }
+        // nibbles 4jw .. 4jw+3: dword jw / 2, bytes 2 (jw % 2) and 2 (jw % 2) + 1
+        const uint32_t prev = (jw & 1) ? (uint32_t)pb[jw >> 1] : 0u;
+        uint32_t wd = e2m1x2_into(prev, p0 * inv_mx, p1 * inv_mx, 2 * (jw & 1));
+        wd = e2m1x2_into(wd, p2 * inv_mx, p3 * inv_mx, 2 * (jw & 1) + 1);
+        pb[jw >> 1] = (int)wd;
+      } else {
+        pb[jw] = I8V ? (int)p_u8x4(p0, p1, p2, p3) : (int)e4m3x4(p0, p1, p2, p3);
       }
     }
+    if constexpr (P4) {
+#pragma unroll
+      for (int k = 4; k < 8; ++k) pb[k] = 0;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int mb = 0; mb < C::MB_O; ++mb) {
+      const i32x8 a = vt_load(lv, mb);
+      if constexpr (I8V) {
+        i32x16 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[0], a[1], a[2], a[3]},
+                                                           i32x4{pb[0], pb[1], pb[2], pb[3]}, i32x16{}, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[4], a[5], a[6], a[7]},
+                                                    i32x4{pb[4], pb[5], pb[6], pb[7]}, acc, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[mb][j] += (float)acc[j];  // |acc| < 64 * 127^2 < 2^24: exact
+      } else if constexpr (P4) {
+        o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 4, 0, 127, 0, e_mx + 127);
+      } else {
+        o[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o[mb], 0, 0, 0, 127, 0, 127);
+      }
+    }
+  };
+
+  if (T > 0) issue_tile(0, k0s, v0s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < T; t += 2) {
+    tile(t, k0s, v0s, k1s, v1s);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) {
-      st.store<P4>(lk, lv, lks, tid, true);
+    if (t + 1 < T) {
+      tile(t + 1, k1s, v1s, k0s, v0s);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
 
   const float l_tot = pair_sum(l_run);
-  const float f = I8V ? *VS / (127.f * l_tot) : *VS / l_tot;
+  const float f = l_tot > 0.f ? (I8V ? *VS / (127.f * l_tot) : *VS / l_tot) : 0.f;
   if (qrow < Nq) {
     uint16_t* dst = O + (qbase + qrow) * C::D;
 #pragma unroll
@@ -645,31 +661,41 @@ __global__ __launch_bounds__(256, 2) void prefill_q8_kernel(
   }
 }
 
-// Test hooks: the scores of one head through the kernels' own tile routines,
-// exact int32 through qk_tile_i8 (F8 false) or fp32 through qk_tile_f8 on
-// E4M3 codes (F8 true).
+// Test hooks: the scores of one head through the forward's own tile routine
+// and LDS layout, exact int32 (F8 false) or fp32 from E4M3 codes (F8
+// true).  One workgroup of 4 waves per (128 queries, 64 keys).
 template <bool F8>
 __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ Q8, const int8_t* __restrict__ K8,
                                                        void* __restrict__ Sv, int Nq, int Nk) {
   using C = Q8Cfg;
-  __shared__ __attribute__((aligned(16))) char lk[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char lk[C::KBUF];
   const int q0 = blockIdx.x * C::BM, kv0 = blockIdx.y * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int qrow = q0 + 32 * w + l32;
+  const auto rk = make_rsrc(K8, (uint32_t)Nk * C::D);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // 8 KB tile: 2 loads of 1 KB per wave
+    const int R = (2 * w + i) * C::RPI + lane / C::SPR, slot = lane % C::SPR;
+    q8_load_lds16(rk, lk + 1024 * (2 * w + i),
+                  (uint32_t)(kv0 + k8_row_key(R)) * C::ROWB + 16 * (slot ^ k8_swz(R)));
+  }
   i32x4 qop[C::KSTEPS];
-  load_q8_operand(Q8 + (size_t)qrow * C::D, qrow < Nq, h, qop);
-  Q8Stage st;
-  st.load(K8, nullptr, nullptr, kv0, Nk, tid, false);
-  st.store(lk, nullptr, nullptr, tid, false);
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    i32x4 x = {0, 0, 0, 0};
+    if (qrow < Nq) x = reinterpret_cast<const i32x4*>(Q8 + (size_t)qrow * C::D)[2 * kk + h];
+    qop[kk] = x;
+  }
+  uint32_t ka_off[C::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) ka_off[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ k8_swz(l32));
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   using Acc = typename std::conditional<F8, f32x16, i32x16>::type;
   using Out = typename std::conditional<F8, float, int32_t>::type;
   Acc acc[2];
-  if constexpr (F8)
-    qk_tile_f8(lk, qop, l32, h, acc);
-  else
-    qk_tile_i8(lk, qop, l32, h, acc);
+  qk_tile<F8>(lk, qop, ka_off, acc);
   Out* S = static_cast<Out*>(Sv);
   if (qrow < Nq) {
 #pragma unroll
@@ -725,8 +751,8 @@ hipError_t launch_prefill_q8(const void* q8v, const void* k8v, const void* v8v, 
   const int var = (int)variant;
 #define ATTN_Q8(CA_, VAR_)                                                                                     \
   if (causal == CA_ && var == VAR_)                                                                            \
-    hipLaunchKernelGGL((prefill_q8_kernel<CA_, VAR_>), dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8,    \
-                       q_scale, k_scale, v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb, \
+    hipLaunchKernelGGL((prefill_q8_kernel<CA_, VAR_>), dim3(total), dim3(Q8Cfg::NT), 0, stream, q8, k8, v8,     \
+                       q_scale, k_scale, v_scale, static_cast<uint16_t*>(out), lse, Nq, Nk, scale * kLog2e, nqb,   \
                        total);
   ATTN_Q8(true, 0)
   ATTN_Q8(false, 0)
