@@ -374,10 +374,10 @@ const char* attn_status_str(int status) {
 }
 
 const char* attn_build_info(void) {
-  return "libattn_mi355x: gfx950; prefill bf16/fp16 d={64,128} BM=256 (8 waves, 2 groups ping-ponging MFMA and "
-         "softmax phases, 32 rows/wave), BN=64 (d=128) / 128 (d=64, half of P formed inside the MFMA phase), "
-         "direct-to-LDS K/V tiles, 32x32x16 MFMA, S^T=KQ^T, V^T via ds_read_b64_tr_b16, running max raised only when "
-         "a lane's tile P sums past 2^14, causal blocks paired on large grids; "
+  return "libattn_mi355x: gfx950; prefill bf16/fp16 d=128 BM=256 (8 waves, 2 groups ping-ponging MFMA and "
+         "softmax phases, 32 rows/wave), BN=64, causal blocks paired on large grids; d=64 BM=128 BN=64 (4 waves, "
+         "3 workgroups/CU interleaving MFMA and softmax freely); direct-to-LDS double-buffered K/V tiles, 32x32x16 "
+         "MFMA, S^T=KQ^T, V^T via ds_read_b64_tr_b16, running max raised only when a lane's tile P sums past 2^14; "
          "decode split-KV 256 threads, 8 rows in flight/lane + LSE merge (static 8 MiB scratch variant); "
          "q8 prefill d=128 BM=128 BN=64 (3 workgroups/CU, double-buffered direct-to-LDS K8/V8 tiles), int8 32x32x32 + "
          "fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8; "

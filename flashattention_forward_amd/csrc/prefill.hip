@@ -12,7 +12,8 @@
 // deferred to the end.  Causal blocks stop at the diagonal ("Causal
 // masking": tiles holding only future keys are never loaded).
 //
-// gfx950 mapping (one workgroup = 8 waves = 256 query rows, key tiles of 64):
+// gfx950 mapping, d = 128 (one workgroup = 8 waves = 256 query rows, key tiles
+// of 64; d = 64 runs the interleaved kernel further below):
 //   * S^T = K Q^T on 32x32x16 MFMA: the K tile (LDS) is the A operand and the
 //     wave's Q rows (VGPRs, loaded once) the B operand.  Working on S^T puts
 //     one query per lane (16 keys in each of lanes l and l^32), so the row
@@ -72,10 +73,6 @@ struct PrefillCfg {
   static constexpr int MB_O = D / 32;        // 32-row blocks of O^T
   static constexpr int NA = NB * KSTEPS;     // MFMAs of S^T per tile
   static constexpr int NC = NG * MB_O;       // MFMAs of O^T per tile
-  // half of P(t) formed inside the GEMM phase (d = 64, where the softmax is the
-  // longer phase: twice the scores per MFMA of d = 128); at d = 128 the GEMM
-  // phase is the longer one and the softmax stays whole in its own phase
-  static constexpr bool EARLY = D == 64;
   static_assert(NA == NC, "S and PV MFMA streams are interleaved one to one");
   static_assert(NA % NLD == 0, "loads are spread evenly over the MFMA steps");
 };
@@ -292,26 +289,15 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         const int kv0 = t * C::BN;
         return (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
       };
-      float lsum_a = 0.f;  // this lane's sum over the first half of P(t), formed during G_t
 
       // ---- G_t: S(t) (t < T) and O += P(t-1) V(t-1) (t >= 1), MFMA streams interleaved;
       // lk holds K(t), lv holds V(t-1).  With LD (group 0) it also issues the loads
       // of K(t+1) into ldk and V(t) into ldv, one every STEP MFMA steps, so that the
       // address unit sees a steady trickle rather than every wave's loads at once.
       // K(t+1) is loaded even when t+1 = T: those rows read as 0 or are never used.
-      // S(t) is formed key block by key block and P(t-1) is consumed group by group,
-      // so after half the steps the first half of S(t) is final and the first half
-      // of the P operand registers is free.  With EARLY the first half of P(t) is
-      // then formed against the running max, its vector instructions interleaved
-      // with the remaining MFMAs (the softmax phase takes it over, or forms it
-      // again, when the tile is masked, has no running max yet, or overflows the
-      // bound).
       auto gemm_phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool LD, int t, const char* lk, const char* lv,
                             char* ldk, char* ldv) {
         constexpr int STEP = C::NA / C::NLD;
-        // vector instructions of the half softmax per remaining MFMA step (about 27
-        // per 16-key group: 8 FMA, 8 exp2, 7 adds, 4 conversions)
-        constexpr int kValuPerStep = (27 * (C::NG / 2) + C::NA / 2 - 1) / (C::NA / 2);
         const bool do_s = t < T, do_pv = t >= 1;
         if (do_s && do_pv) {
 #pragma unroll
@@ -323,8 +309,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             ka[i] = ka_load(lk, i);
             va[i] = va_load(lv, i);
           }
-          const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-          (void)m_ref;
 #pragma unroll
           for (int i = 0; i < C::NA; ++i) {
             const op8 a = ka[i % PF], b = va[i % PF];
@@ -335,11 +319,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             s[i / C::KSTEPS] = M::mma(a, qop[i % C::KSTEPS], s[i / C::KSTEPS]);
             o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
             if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
-            if (C::EARLY && i == C::NA / 2 - 1) lsum_a = exps_half(0, m_ref);
           }
           // issue order: the first PF steps' operand reads, then per step its two
-          // MFMAs each followed by the reads of the step PF ahead, then its load;
-          // in the second half of the steps the half softmax fills the gaps
+          // MFMAs each followed by the reads of the step PF ahead, then its load
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3 * PF, 0);
 #pragma unroll
           for (int i = 0; i < C::NA; ++i) {
@@ -348,7 +330,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             if (i + PF < C::NA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
             if (LD && i % STEP == STEP - 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-            if (C::EARLY && i >= C::NA / 2) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerStep, 0);
           }
         } else if (do_s) {
 #pragma unroll
@@ -405,14 +386,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         // a lane's probabilities would sum past kMaxTileSum.  Then the running max
         // is raised to the row max, O and l are rescaled, and P(t) is formed again.
         const bool first = __any(m_run == -INFINITY);
-        // the first half of P(t) formed during G_t stands unless the tile was masked
-        // here afterwards, G_t had no P(t-1) to consume (t = 0), or the max is raised
-        const bool have_a = C::EARLY && t >= 1 && !edge && !first;
         float tot = 0.f;
         bool raise = first;
         if (!first) {
-          const float a = have_a ? lsum_a : exps_half(0, m_run);
-          tot = a + exps_half(1, m_run);
+          tot = exps_half(0, m_run) + exps_half(1, m_run);
           // not (tot <= bound) also catches an overflow to inf
           raise = __any(!(tot <= kMaxTileSum));
         }
@@ -543,6 +520,246 @@ static hipError_t launch_t(const void* q, const void* k, const void* v, void* ou
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Interleaved schedule for d = 64, where the softmax (two vector instructions
+// or more per score, exponentials at a quarter of the rate) outweighs the
+// matrix work.  A workgroup is 4 waves of 32 query rows; each wave runs S(t),
+// the softmax and O += P(t) V(t) in turn, and three workgroups share a CU
+// (three waves per SIMD), so the waves of a SIMD interleave their matrix and
+// vector work freely.  K/V tiles of 64 keys go from global memory straight
+// into double-buffered LDS (layouts and swizzles as in the ping-pong kernel);
+// tile t+1 is requested at the start of tile t, one barrier per tile.
+template <int D>
+struct FiCfg {
+  static constexpr int BM = 128;             // query rows per workgroup: 4 waves x 32
+  static constexpr int BN = 64;              // keys per tile
+  static constexpr int NT = 256;
+  static constexpr int NB = BN / 32;         // 32-key blocks of S^T per tile
+  static constexpr int NG = BN / 16;         // 16-key groups (k-steps of O^T) per tile
+  static constexpr int ROWB = D * 2;
+  static constexpr int SPR = ROWB / 16;
+  static constexpr int TILEB = BN * ROWB;
+  static constexpr int RPI = 1024 / ROWB;
+  static constexpr int LPW = TILEB / 1024 / 4;  // 1 KB loads per K or V tile for each wave
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int MB_O = D / 32;
+  static constexpr int NA = NB * KSTEPS;     // MFMAs of S^T per tile
+  static constexpr int NC = NG * MB_O;       // MFMAs of O^T per tile
+};
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(256, 3) void prefill_fi_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, SeqShape sh, float c, int nqb, int total) {
+  using C = FiCfg<D>;
+  using M = Mfma<BF16>;
+  typedef typename M::op8 op8;
+  typedef typename M::op2 op2;
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILEB];
+
+  // work item: one 128-row query block of one (sequence, head), longest first
+  // when causal; dense batches give each XCD a contiguous range of heads,
+  // packed batches take block rank j slowest over all (sequence, head) pairs
+  const bool packed = sh.cu_q != nullptr;
+  const int logical = packed ? (int)blockIdx.x : xcd_remap(blockIdx.x, total);
+  int bh, j_item;
+  if (packed) {
+    const int nh = total / nqb;
+    j_item = logical / nh;
+    bh = logical - j_item * nh;
+  } else {
+    bh = logical / nqb;
+    j_item = logical - bh * nqb;
+  }
+  const int qb = CAUSAL ? nqb - 1 - j_item : j_item;
+  const SeqSpan sp = seq_span(sh, bh / sh.H, bh % sh.H);
+  const int Nq = sp.nq, Nk = sp.nk;
+  const int off = Nk - Nq;
+  const int q0 = qb * C::BM;
+  if (q0 >= Nq) return;  // past a short packed sequence (uniform over the workgroup)
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t qbase = sp.q_row0 * D;
+  const size_t kbase = sp.k_row0 * D;
+  const auto rq = make_rsrc(Q + qbase, (uint32_t)Nq * D * 2);
+  const auto rk = make_rsrc(K + kbase, (uint32_t)Nk * D * 2);
+  const auto rv = make_rsrc(V + kbase, (uint32_t)Nk * D * 2);
+
+  uint32_t gk_off[C::LPW], gv_off[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int row = (C::LPW * w + i) * C::RPI + lane / C::SPR, slot = lane % C::SPR;
+    gk_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ k_swz<D>(row));
+    gv_off[i] = (uint32_t)row * C::ROWB + 16 * (slot ^ v_swz<D>(row));
+  }
+  auto issue_tile = [&](int t, char* ldk, char* ldv) {
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      tile_load_lds(rk, ldk + 1024 * (C::LPW * w + i), (uint32_t)t * C::TILEB + gk_off[i]);
+      tile_load_lds(rv, ldv + 1024 * (C::LPW * w + i), (uint32_t)t * C::TILEB + gv_off[i]);
+    }
+  };
+  uint32_t ka_off[C::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) ka_off[kk] = l32 * C::ROWB + 16 * ((2 * kk + h) ^ k_swz<D>(l32));
+  const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+  const int vrow = (r16 >> 2) + 4 * h;
+  uint32_t va_off[C::MB_O];
+#pragma unroll
+  for (int mb = 0; mb < C::MB_O; ++mb) {
+    const int col = 32 * mb + 16 * g1 + 4 * (r16 & 3);
+    va_off[mb] = vrow * C::ROWB + 16 * ((col >> 3) ^ v_swz<D>(vrow)) + 2 * (col & 7);
+  }
+  auto ka_load = [&](const char* lk, int i) {  // K operand of S^T step i: key block i/KSTEPS, k-step i%KSTEPS
+    return lds_load<op8>(lk, ka_off[i % C::KSTEPS] + (i / C::KSTEPS) * 32 * C::ROWB);
+  };
+  auto va_load = [&](const char* lv, int j) {  // V^T operand of O^T step j: 16-key group j/MB_O, d block j%MB_O
+    const uint32_t a0 = va_off[j % C::MB_O] + 16 * (j / C::MB_O) * C::ROWB;
+    const s16x4 lo = lds_read_tr16(lv, a0);
+    const s16x4 hi = lds_read_tr16(lv, a0 + 8 * C::ROWB);
+    return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  const int qmin_w = q0 + 32 * w;
+  const int qrow = qmin_w + l32;
+  op8 qop[C::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk)
+    qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)qrow * C::ROWB + (16 * kk + 8 * h) * 2));
+
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
+  const int T = max(0, (kv_end + C::BN - 1) / C::BN);
+
+  f32x16 o[C::MB_O];
+#pragma unroll
+  for (int mb = 0; mb < C::MB_O; ++mb) o[mb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto tile = [&](int t, const char* lk, const char* lv, char* ldk, char* ldv) {
+    if (t + 1 < T) issue_tile(t + 1, ldk, ldv);
+    const int kv0 = t * C::BN;
+    if (CAUSAL && kv0 > qmin_w + 31 + off) return;  // no key of the tile is visible to this wave
+    f32x16 s[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < C::NA; ++i) s[i / C::KSTEPS] = M::mma(ka_load(lk, i), qop[i % C::KSTEPS], s[i / C::KSTEPS]);
+    const bool edge = (kv0 + C::BN > Nk) || (CAUSAL && kv0 + C::BN - 1 > qmin_w + off);
+    if (edge) {
+      // element i of block nb holds key kv0 + 4h + 32 nb + 8 (i/4) + i%4 (bit blend as in prefill_kernel)
+      const int lim = min(Nk - 1, CAUSAL ? qrow + off : Nk - 1) - (kv0 + 4 * h);
+      constexpr uint32_t kNegInf = 0xFF800000u;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = 32 * nb + 8 * (i >> 2) + (i & 3);
+          const uint32_t hide = (uint32_t)((lim - e) >> 31);
+          const float v = s[nb][i];
+          const uint32_t bits = __builtin_bit_cast(uint32_t, v);
+          s[nb][i] = __builtin_bit_cast(float, (bits & ~hide) | (kNegInf & hide));
+        }
+    }
+    op8 pb[C::NG];
+    // P(t) against m_ref into pb; this lane's sum of it
+    auto exps = [&](float m_ref) {
+      float lsum[4];
+#pragma unroll
+      for (int g = 0; g < C::NG; ++g) {
+        const int nb = g >> 1, tt = g & 1;
+        op2 pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j], c, -m_ref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * tt + 2 * j + 1], c, -m_ref));
+          pr[j] = M::pack2(p0, p1);
+          lsum[j] = g == 0 ? p0 + p1 : lsum[j] + (p0 + p1);
+        }
+        pb[g] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                        __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    // the running max is raised only on a row's first tile or when a lane's P
+    // would sum past kMaxTileSum, as in prefill_kernel
+    const bool first = __any(m_run == -INFINITY);
+    float tot = 0.f;
+    bool raise = first;
+    if (!first) {
+      tot = exps(m_run);
+      raise = __any(!(tot <= kMaxTileSum));
+    }
+    if (raise) {
+      float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int i = nb == 0 ? 2 : 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
+      const float m_new = fmaxf(m_run, pair_max(mx) * c);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int mb = 0; mb < C::MB_O; ++mb) o[mb] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      tot = exps((m_run == -INFINITY) ? 0.f : m_run);
+    }
+    l_run += tot;
+#pragma unroll
+    for (int j = 0; j < C::NC; ++j) o[j % C::MB_O] = M::mma(va_load(lv, j), pb[j / C::MB_O], o[j % C::MB_O]);
+  };
+
+  if (T > 0) issue_tile(0, k0s, v0s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < T; t += 2) {
+    tile(t, k0s, v0s, k1s, v1s);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < T) {
+      tile(t + 1, k1s, v1s, k0s, v0s);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < Nq) {
+    uint16_t* dst = O + qbase + (size_t)qrow * D;
+#pragma unroll
+    for (int mb = 0; mb < C::MB_O; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const op2 x0 = M::pack2(o[mb][4 * g + 0] * inv, o[mb][4 * g + 1] * inv);
+        const op2 x1 = M::pack2(o[mb][4 * g + 2] * inv, o[mb][4 * g + 3] * inv);
+        u32x2 u;
+        u[0] = __builtin_bit_cast(uint32_t, x0);
+        u[1] = __builtin_bit_cast(uint32_t, x1);
+        *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g + 4 * h) = u;
+      }
+    if (LSE != nullptr && h == 0) LSE[sp.q_row0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+template <int D, bool BF16, bool CAUSAL>
+static hipError_t launch_fi(const void* q, const void* k, const void* v, void* out, float* lse, const SeqShape& sh,
+                            int nseq, int max_nq, float scale, hipStream_t stream) {
+  using C = FiCfg<D>;
+  const int nqb = (max_nq + C::BM - 1) / C::BM;
+  const int total = nqb * nseq * sh.H;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_fi_kernel<D, BF16, CAUSAL>), dim3(total), dim3(C::NT), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse, sh, scale * kLog2e, nqb,
+                     total);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* out, float* lse, const SeqShape& sh,
                           int nseq, int max_nq, int d, float scale, bool causal, bool bf16, hipStream_t stream) {
 #define ATTN_DISPATCH(D_, BF_, CA_)          \
@@ -552,10 +769,10 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* out
   ATTN_DISPATCH(128, true, true)
   ATTN_DISPATCH(128, false, false)
   ATTN_DISPATCH(128, false, true)
-  ATTN_DISPATCH(64, true, false)
-  ATTN_DISPATCH(64, true, true)
-  ATTN_DISPATCH(64, false, false)
-  ATTN_DISPATCH(64, false, true)
+  if (d == 64 && bf16 == true && causal == false) return launch_fi<64, true, false>(q, k, v, out, lse, sh, nseq, max_nq, scale, stream);
+  if (d == 64 && bf16 == true && causal == true) return launch_fi<64, true, true>(q, k, v, out, lse, sh, nseq, max_nq, scale, stream);
+  if (d == 64 && bf16 == false && causal == false) return launch_fi<64, false, false>(q, k, v, out, lse, sh, nseq, max_nq, scale, stream);
+  if (d == 64 && bf16 == false && causal == true) return launch_fi<64, false, true>(q, k, v, out, lse, sh, nseq, max_nq, scale, stream);
 #undef ATTN_DISPATCH
   return hipErrorInvalidValue;
 }
