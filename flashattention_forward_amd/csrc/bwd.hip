@@ -328,12 +328,18 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * a + b;
-          float p = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -Lr[b]));
-          if (edge) {
-            const int qi = q0 + 8 * a + 4 * h + b;
-            if (qi >= Nq || (CAUSAL && key > qi + off)) p = 0.f;
-          }
-          sv[i] = p;
+          sv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -Lr[b]));
+        }
+      }
+      // masked pairs (query past Nq, or key after the query on causal tiles)
+      // only on edge steps: a uniform branch, so other steps carry no selects
+      if (edge) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = q0 + 8 * (i >> 2) + 4 * h + (i & 3);
+          const uint32_t hide = (qi >= Nq || (CAUSAL && key > qi + off)) ? 0xFFFFFFFFu : 0u;
+          const float v = sv[i];  // copied out first (a bit cast of a vector element in place misreads)
+          sv[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & ~hide);
         }
       }
       pa[0] = pack8<M>(sv, 0);
@@ -513,14 +519,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     // element i: key j0 + 8 (i/4) + 4h + i%4 of this lane's query
     const bool edge = (j0 + C::BS > Nk) || (CAUSAL && j0 + 31 > qw0 + off);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -Lq));
-      if (edge) {
+    for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -Lq));
+    // masked pairs only on edge steps (a uniform branch, as in bwd_kv)
+    if (edge) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
         const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (kj >= Nk || (CAUSAL && kj > query + off)) p = 0.f;
+        const uint32_t hide = (kj >= Nk || (CAUSAL && kj > query + off)) ? 0xFFFFFFFFu : 0u;
+        const float v = s[i];
+        s[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & ~hide);
       }
-      dp[i] = p * (dp[i] - Dq);
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dp[i] = s[i] * (dp[i] - Dq);
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
       const op8 da = pack8<M>(dp, 8 * ti);
