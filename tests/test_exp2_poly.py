@@ -40,7 +40,8 @@ def emulate(x, c=None, flip=False):
     x = np.asarray(x, np.float32)
     xc = np.maximum(x, np.float32(-125.0))
     n = np.floor(xc).astype(np.float32)
-    f = (n - xc if flip else xc - n).astype(np.float32)
+    with np.errstate(invalid="ignore"):  # x = +inf gives inf - inf here; the select below returns inf
+        f = (n - xc if flip else xc - n).astype(np.float32)
     k = lambda v: np.full(f.shape, v, np.float32)
     p = _fma32(_fma32(_fma32(k(c[3]), f, k(c[2])), f, k(c[1])), f, k(c[0]))
     r = (p.view(np.int32) + (np.minimum(n, 127).astype(np.int32) << 23)).view(np.float32)
