@@ -31,9 +31,10 @@
  *     Nq > Nk is rejected.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and the call returns without synchronising.  The library never
- *     allocates or frees device memory and keeps no mutable global state:
- *     calls are reentrant and thread-safe.  Asynchronous GPU faults surface
- *     at the caller's next synchronisation.
+ *     allocates or frees device memory and, apart from the static split
+ *     array of attn_fwd_decode_static (below), keeps no mutable global
+ *     state: the other calls are reentrant and thread-safe.  Asynchronous
+ *     GPU faults surface at the caller's next synchronisation.
  *   - Every argument is validated before anything is launched: a return of
  *     ATTN_E_INVALID, ATTN_E_UNSUPPORTED or ATTN_E_WORKSPACE means nothing
  *     was launched.  ATTN_E_HIP reports a launch error; the entry points
