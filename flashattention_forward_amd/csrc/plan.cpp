@@ -17,14 +17,14 @@ int decode_heads_per_workgroup(int H, int Hkv) {
 
 int decode_default_splits(int B, int H, int Hkv, int Nk, int d) {
   (void)d;
-  // aim for about 8192 (query head, key range) streams with at least 128 keys
+  // aim for about 4096 (query head, key range) streams with at least 128 keys
   // each.  A grouped workgroup serves several heads of a range at once; counting
   // streams per query head still measured best for it (splitting its key range
   // further only added partial states to write and merge)
   (void)Hkv;
   long bh = (long)B * H;
   int s = 1;
-  while (bh * s < 8192 && s < 256 && (long)(s * 2) * 128 <= Nk) s *= 2;
+  while (bh * s < 4096 && s < 256 && (long)(s * 2) * 128 <= Nk) s *= 2;
   return s;
 }
 

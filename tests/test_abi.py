@@ -222,7 +222,9 @@ def test_gqa_and_varlen_reject():
     assert gqa(Hkv=0) == Bd.ATTN_E_INVALID
     assert gqa(d=80) == Bd.ATTN_E_UNSUPPORTED
     assert gqa(Nq=1) == Bd.ATTN_E_WORKSPACE           # decode needs its workspace
-    assert L.attn_fwd_gqa_workspace_bytes(64, 32, 8, 1, 8192, 128, 0) == 64 * 32 * 4 * 129 * 4
+    s = L.attn_fwd_decode_splits(64, 32, 8192, 128)
+    assert s == 2                                     # 4096 (head, key range) streams, >= 128 keys each
+    assert L.attn_fwd_gqa_workspace_bytes(64, 32, 8, 1, 8192, 128, 0) == 64 * 32 * s * 129 * 4
     assert L.attn_fwd_gqa_workspace_bytes(64, 32, 32, 1, 8192, 128, 0) == L.attn_fwd_workspace_bytes(
         64, 32, 1, 8192, 128, 0)
     assert L.attn_fwd_gqa_workspace_bytes(1, 6, 4, 1, 100, 128, 0) == 0      # H not a multiple of Hkv
