@@ -13,8 +13,10 @@
 //   bwd_pre: per query row, (LSE log2 e, D) into a float2 workspace;
 //   bwd_kv:  a workgroup owns 128 keys (32 per wave, K and V held in registers
 //            as MFMA operands) and streams the queries in steps of 32 through
-//            LDS (Q, dO tiles and their (LSE, D) pairs, double-buffered,
-//            loaded straight into LDS).  Per step and wave: S = Q K^T and
+//            LDS (Q and dO tiles, and the step's 32 LSE values followed by
+//            its 32 D values, double-buffered, loaded straight into LDS, so
+//            a lane reads the four it needs at a time in one 16-byte read).
+//            Per step and wave: S = Q K^T and
 //            dP = dO V^T come out with one key per lane, which is exactly the
 //            A-operand layout of P^T and dS^T, so dV += P^T dO and
 //            dK += dS^T Q follow with dO and Q read transposed from LDS;
@@ -228,7 +230,9 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
       bwd_load_lds16(rq, qt + 1024 * (C::LPW * w + i), base + goff[i]);
       bwd_load_lds16(rdo, dt + 1024 * (C::LPW * w + i), base + goff[i]);
     }
-    if (w == 0) bwd_load_lds4(rld, lt, (uint32_t)(st * C::BS) * 8 + 4 * lane);
+    // lane i < 32 fetches row i's LSE, lane 32 + i its D: the tile holds 32
+    // LSE values, then 32 D values
+    if (w == 0) bwd_load_lds4(rld, lt, (uint32_t)(st * C::BS + (lane & 31)) * 8 + 4 * (lane >> 5));
   };
   // row reads (A operand: m = query l32, k = d 16 kk + 8h .. +7): byte offset
   // l32 ROWB + ((32 kk + 16 h) ^ 16 swz(l32)), one XOR-add per read
@@ -322,9 +326,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
       f32x16 sv = row_gemm(std::false_type{}, qt, kop, nullptr, f32x16{});
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 x0 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8);
-        const f32x4 x1 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8 + 16);
-        const float Lr[4] = {x0[0], x0[2], x1[0], x1[2]};
+        const f32x4 Lr = lds_load<f32x4>(lt, (8 * a + 4 * h) * 4);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * a + b;
@@ -356,9 +358,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
       f32x16 dpv = row_gemm(std::integral_constant<bool, VLDS>{}, dt, vop, vw, f32x16{});
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 x0 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8);
-        const f32x4 x1 = lds_load<f32x4>(lt, (8 * a + 4 * h) * 8 + 16);
-        const float Dr[4] = {x0[1], x0[3], x1[1], x1[3]};
+        const f32x4 Dr = lds_load<f32x4>(lt, 4 * C::BS + (8 * a + 4 * h) * 4);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * a + b;
