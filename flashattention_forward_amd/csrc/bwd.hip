@@ -75,6 +75,17 @@ __device__ __forceinline__ typename M::op8 pack8(const f32x16& x, int base) {
                                  0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// element j of a packed 16-bit operand, widened to fp32 (exact): bf16 by
+// moving its bits into the high half of the word, fp16 by conversion
+template <class M>
+__device__ __forceinline__ float op8_elem(typename M::op8 v, int j) {
+  const uint32_t dw = __builtin_bit_cast(u32x4, v)[j >> 1];
+  if constexpr (std::is_same<typename M::op8, bf16x8>::value)
+    return __builtin_bit_cast(float, (j & 1) ? (dw & 0xffff0000u) : (dw << 16));
+  else
+    return (float)__builtin_bit_cast(typename M::op2, dw)[j & 1];
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint16_t to_half_bits(float x) {
   typedef typename Mfma<BF16>::op2 op2;
@@ -362,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * a + b;
-          const float p = (float)pa[i >> 3][i & 7];
+          const float p = op8_elem<M>(pa[i >> 3], i & 7);
           dpv[i] = p * (dpv[i] - Dr[b]);
         }
       }

@@ -251,6 +251,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       int kv_end = Nk;
       if (CAUSAL) kv_end = min(Nk, min(q0 + C::BM, Nq) - 1 + off + 1);
       const int T = max(0, (kv_end + C::BN - 1) / C::BN);  // 0: no key visible to the block
+      // tiles this wave group's rows can see: on a causal block the first group
+      // (the block's first 128 rows) stops up to two tiles before the second
+      int Tg = T;
+      if (CAUSAL) Tg = min(T, max(0, (min(Nk, min(q0 + 128 * grp + 128, Nq) + off) + C::BN - 1) / C::BN));
 
       f32x16 o[C::MB_O];
 #pragma unroll
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       auto gemm_phase = [&](const Rsrc& rk_, const Rsrc& rv_, bool LD, int t, const char* lk, const char* lv,
                             char* ldk, char* ldv) {
         constexpr int STEP = C::NA / C::NLD;
-        const bool do_s = t < T, do_pv = t >= 1;
+        const bool do_s = t < (CAUSAL ? Tg : T), do_pv = t >= 1 && (!CAUSAL || t <= Tg);
         if (do_s && do_pv) {
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) s[nb] = f32x16{};
@@ -344,21 +348,30 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
             s[i / C::KSTEPS] = M::mma(a, qop[i % C::KSTEPS], s[i / C::KSTEPS]);
             if (LD && i % STEP == STEP - 1) issue_load(rk_, rv_, i / STEP, ldk, ldv, t + 1, t);
           }
-        } else if (do_pv) {
-          op8 va[2];
-          va[0] = va_load(lv, 0);
-          va[1] = va_load(lv, 1);
+        } else {
+          // past this group's last tile the loading group still fetches the
+          // other group's tiles
+          if (CAUSAL && LD && t < T) {
 #pragma unroll
-          for (int i = 0; i < C::NC; ++i) {
-            const op8 b = va[i & 1];
-            if (i + 2 < C::NC) va[i & 1] = va_load(lv, i + 2);
-            o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
+            for (int q = 0; q < C::NLD; ++q) issue_load(rk_, rv_, q, ldk, ldv, t + 1, t);
+          }
+          if (do_pv) {
+            op8 va[2];
+            va[0] = va_load(lv, 0);
+            va[1] = va_load(lv, 1);
+#pragma unroll
+            for (int i = 0; i < C::NC; ++i) {
+              const op8 b = va[i & 1];
+              if (i + 2 < C::NC) va[i & 1] = va_load(lv, i + 2);
+              o[i % C::MB_O] = M::mma(b, pb[i / C::MB_O], o[i % C::MB_O]);
+            }
           }
         }
       };
 
       // ---- X_t: mask, running max, rescale, P(t) = exp2(S c - m), row sum
       auto softmax_phase = [&](int t) {
+        if (CAUSAL && t >= Tg) return;
         const int kv0 = t * C::BN;
         const bool edge = edge_tile(t);
         if (edge) {
