@@ -23,7 +23,7 @@ Printed as ONE JSON line, which also carries
     with P in MXFP4), each timed the same way (informational).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                       [--copy-calibration] [--decode-only]
+                       [--copy-calibration] [--decode-only | --long-only | --quant-only | --backward-only]
        python bench.py --traffic-from FETCH_DIR WRITE_DIR
        python bench.py --mfma-from DIR
        python bench.py --decode-traffic-from FETCH_DIR WRITE_DIR
@@ -404,6 +404,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--quant-only", action="store_true")
     ap.add_argument("--long-only", action="store_true", help="the long causal sequence alone (counter runs)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="the non-causal backward of the prefill workload alone (counter runs)")
     ap.add_argument("--rescale-stats", action="store_true",
                     help="CPU only: how often each max-raising rule rescales, on the bench inputs")
     args = ap.parse_args()
@@ -454,6 +456,18 @@ def main():
         _, per = timed_launches([lambda: F.attn_fwd(tq, tk, tv, causal=True, scale=wl.scale, out=o, lse=l)],
                                 args.steps, args.warmup)
         print(json.dumps({"workload": "long_23400_causal", "ms": round(per[0] * 1e3, 4)}))
+        return
+    if args.backward_only:
+        # the non-causal backward of prefill_4k alone (for its counter runs)
+        w = G.WORKLOADS["prefill_4k"]
+        tq, tk, tv = (G.to_torch(x, "bf16") for x in G.draw_qkv(w, threads=16))
+        tdo = G.to_torch(G.draw_tensor(w, "do", threads=16), "bf16")
+        o, l = F.attn_fwd(tq, tk, tv, causal=False, scale=w.scale)
+        dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(w.B * w.H * w.Nq * 8, device="cuda", dtype=torch.uint8)
+        _, per = timed_launches([lambda: F.attn_bwd(tq, tk, tv, o, tdo, l, causal=False, scale=w.scale, dq=dq, dk=dk,
+                                                    dv=dv, workspace=ws)], args.steps, args.warmup)
+        print(json.dumps({"workload": "backward_4k", "ms": round(per[0] * 1e3, 4)}))
         return
     if args.quant_only:
         # the quantised forward of quant_8k alone (int8 scores, E4M3 P.V; for its counter runs)
