@@ -237,6 +237,19 @@ def timed_launches(fns, steps, warmup):
     return total, per
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(seconds_target: float = 15.0, max_heads: int = 1024):
     """The fp64 oracle on a bounded sample of the prefill workload: whole
     heads, alternating non-causal and causal, until ~seconds_target."""
@@ -261,6 +274,7 @@ def cpu_baseline(seconds_target: float = 15.0, max_heads: int = 1024):
         heads += 1
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{heads} whole heads (alternating non-causal/causal) of B=4 H=32 N=4096 d=128 bf16, "
                       f"fp64 numpy, {dt:.1f} s incl. input generation"}
 
