@@ -38,7 +38,7 @@ the copy.  --traffic-from turns the two runs into profiles/prefill_4k_traffic.js
 
 MFMA utilisation: one rocprofv3 run of the same command with --pmc MfmaUtil
 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE; --mfma-from turns it into
-profiles/prefill_4k_mfma.json.  Decode HBM bytes: the two traffic runs of
+profiles/prefill_4k_mfma.json (both launches).  Decode HBM bytes: the two traffic runs of
     python bench.py --decode-only --steps 3 --warmup 1 --copy-calibration
 and --decode-traffic-from, giving profiles/decode_8k_traffic.json.  Each
 record carries a hash of the kernel source it was taken on and is ignored
@@ -63,6 +63,7 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4k_traffic.json")
 COPY_BYTES = 1 << 30          # bytes read (and written) by one calibration copy
 PREFILL_KERNEL = "prefill_kernel<128, true, false, 0>"   # bf16, non-causal, all exp2 on v_exp_f32
+PREFILL_KERNEL_CAUSAL = "prefill_kernel<128, true, true, 0>"
 MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_4k_mfma.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8k_traffic.json")
 DECODE_KERNELS = ("decode_partial_kernel<128, true, 1>", "decode_merge_kernel")
@@ -164,25 +165,29 @@ def traffic_from(fetch_dir: str, write_dir: str) -> dict:
 
 
 def mfma_from(run_dir: str) -> dict:
-    """MFMA utilisation of the non-causal prefill kernel from one rocprofv3 run
-    with --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE: rocprof's
-    derived MfmaUtil (busy cycles summed over all SIMDs / (active cycles x
-    SIMDs)), the busy cycles per SIMD, and the clock the active-cycle count
-    implies over the dispatch (GRBM_GUI_ACTIVE summed over the 8 XCDs)."""
-    util = [v for k, v in _counter_rows(run_dir, "MfmaUtil") if PREFILL_KERNEL in k]
-    busy = [v for k, v in _counter_rows(run_dir, "SQ_VALU_MFMA_BUSY_CYCLES") if PREFILL_KERNEL in k]
-    gui = [(v, t) for k, v, t in _counter_rows(run_dir, "GRBM_GUI_ACTIVE", True) if PREFILL_KERNEL in k]
-    if not util or not busy or not gui:
-        raise SystemExit(f"no {PREFILL_KERNEL} dispatches under {run_dir}")
-    n = min(len(util), len(busy), len(gui))
-    clocks = [g / 8.0 / t for g, t in gui[:n]]
-    mfmas = 1099511627776.0 / (32 * 32 * 16 * 2)          # 32x32x16 MFMAs per launch
-    rec = {"kernel": PREFILL_KERNEL, "kernel_source_sha": kernel_source_sha(), "dispatches": n,
-           "mfma_util_pct": [round(u, 2) for u in util[:n]],
-           "mfma_busy_cycles_per_simd": [round(b / 1024.0) for b in busy[:n]],
-           "busy_cycles_per_mfma": round(busy[0] / (mfmas), 2),
-           "clock_ghz": [round(c, 3) for c in clocks],
-           "dispatch_us": [round(t / 1e3, 1) for _, t in gui[:n]]}
+    """MFMA utilisation of the prefill kernel from one rocprofv3 run with --pmc
+    MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE: rocprof's derived
+    MfmaUtil (busy cycles summed over all SIMDs / (active cycles x SIMDs)),
+    the busy cycles per SIMD, and the clock the active-cycle count implies
+    over the dispatch (GRBM_GUI_ACTIVE summed over the 8 XCDs); the
+    non-causal launch at the top level, the causal one under "causal"."""
+    def one(kernel: str) -> dict:
+        util = [v for k, v in _counter_rows(run_dir, "MfmaUtil") if kernel in k]
+        busy = [v for k, v in _counter_rows(run_dir, "SQ_VALU_MFMA_BUSY_CYCLES") if kernel in k]
+        gui = [(v, t) for k, v, t in _counter_rows(run_dir, "GRBM_GUI_ACTIVE", True) if kernel in k]
+        if not util or not busy or not gui:
+            raise SystemExit(f"no {kernel} dispatches under {run_dir}")
+        n = min(len(util), len(busy), len(gui))
+        return {"kernel": kernel, "dispatches": n,
+                "mfma_util_pct": [round(u, 2) for u in util[:n]],
+                "mfma_busy_cycles_per_simd": [round(b / 1024.0) for b in busy[:n]],
+                "clock_ghz": [round(g / 8.0 / t, 3) for g, t in gui[:n]],
+                "dispatch_us": [round(t / 1e3, 1) for _, t in gui[:n]]}
+    rec = one(PREFILL_KERNEL)
+    mfmas = 1099511627776.0 / (32 * 32 * 16 * 2)          # 32x32x16 MFMAs per non-causal launch
+    rec = {"kernel": PREFILL_KERNEL, "kernel_source_sha": kernel_source_sha(), **{k: v for k, v in rec.items() if k != "kernel"},
+           "busy_cycles_per_mfma": round(rec["mfma_busy_cycles_per_simd"][0] * 1024.0 / mfmas, 2),
+           "causal": one(PREFILL_KERNEL_CAUSAL)}
     return _write(MFMA_FILE, rec)
 
 
@@ -532,6 +537,7 @@ def main():
                      "flops_per_launch": flops_nc,
                      "mfma_util_counted": None if mf is None else {
                          "pct": mf["mfma_util_pct"], "clock_ghz": mf["clock_ghz"],
+                         "causal_pct": mf.get("causal", {}).get("mfma_util_pct"),
                          "source": "profiles/prefill_4k_mfma.json (rocprofv3 MfmaUtil)"}},
         "kernels": {
             "prefill_noncausal": {"ms": round(per[0] * 1e3, 4), "tflops": round(flops_nc / per[0] / 1e12, 3),
