@@ -46,6 +46,10 @@
 //     step, and the buffer range check turns keys past Nk into zeros.  The
 //     16-byte slots of each LDS row are XOR-swizzled on the load side so the
 //     K operand reads and the transposing V reads hit distinct banks.
+//   * The epilogue writes O through LDS, so that every global store covers
+//     whole 128-byte pieces of rows, and on dense grids it first requests the
+//     workgroup's next item's Q rows and first K tile, which then arrive
+//     while O is written instead of after it.
 //   * Workgroups are renumbered so each XCD walks a contiguous range of
 //     (head, query block) items (K/V of a head stay in that XCD's L2).  A
 //     causal grid with many heads gives each workgroup two query blocks, the
@@ -163,6 +167,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   // persist > 0: a grid of one workgroup per CU walks virtual blocks
   // blockIdx.x, blockIdx.x + gridDim.x, ... (gridDim.x a multiple of 8, so each
   // virtual block stays on its workgroup's XCD); otherwise one block each
+  // the next item's Q operand and first K tile are requested during this item's
+  // epilogue (dense grids): `pre` says they are in flight
+  op8 qop[C::KSTEPS];
+  bool pre = false;
   for (int vb = blockIdx.x; vb < total; vb += persist ? (int)gridDim.x : total) {
     const bool packed = sh.cu_q != nullptr;
     const int logical = packed ? vb : xcd_remap(vb, total);
@@ -240,10 +248,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       // B operand of S^T = K Q^T: lane holds Q[qrow][16kk + 8h .. +7]; rows past Nq read as 0
       const int qmin_w = q0 + 128 * grp + 32 * wg;  // smallest query row of this wave
       const int qrow = qmin_w + l32;
-      op8 qop[C::KSTEPS];
+      if (!pre) {
 #pragma unroll
-      for (int kk = 0; kk < C::KSTEPS; ++kk)
-        qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)qrow * C::ROWB + (16 * kk + 8 * h) * 2));
+        for (int kk = 0; kk < C::KSTEPS; ++kk)
+          qop[kk] = __builtin_bit_cast(op8, buf_load16(rq, (uint32_t)qrow * C::ROWB + (16 * kk + 8 * h) * 2));
+      }
       // keep the Q loads ahead of the first tile's: the in-order load counter then
       // retires them before the first tile is read, and no wait on them lands in the loop
       __builtin_amdgcn_sched_barrier(0);
@@ -431,12 +440,18 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         l_run += tot;
       };
 
-      // prologue: K(0) into LDS
-      if (grp == 0) {
+      // prologue: K(0) into LDS, unless the previous item's epilogue requested it
+      // together with Q; then only the previous item's 8 O stores per wave, issued
+      // after those loads, may still be in flight (vmcnt 8, lgkmcnt 0)
+      if (!pre) {
+        if (grp == 0) {
 #pragma unroll
-        for (int q = 0; q < C::LPG; ++q) issue_load(rk, rv, q, k0s, nullptr, 0, 0);
+          for (int q = 0; q < C::LPG; ++q) issue_load(rk, rv, q, k0s, nullptr, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0078);
       }
-      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
 
       // phase p: group 0 runs phase p of its own sequence G_0 X_0 G_1 X_1 ... G_T,
@@ -480,20 +495,78 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       // a row that saw no key (packed batches only) has l = 0: O = 0, LSE = -inf
       const float l_tot = pair_sum(l_run);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      if (qrow < Nq) {
-        uint16_t* dst = O + qbase + (size_t)qrow * D;
+      // O leaves through LDS, so that every global store writes whole 128-byte
+      // pieces of rows (the accumulator layout gives a lane 8-byte pieces of one
+      // row, 16 bytes apart).  Each wave stages its 32 rows 64 columns at a time
+      // in a private 4 KB region of the V tile buffers, which no wave reads or
+      // loads into between the item's last barrier and the next item's first;
+      // 16-byte chunks are XOR-swizzled by row.
+      static_assert(D % 64 == 0, "O is staged 64 columns at a time");
+      if (qrow < Nq && LSE != nullptr && h == 0) LSE[sp.q_row0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+      // the next item of this workgroup (dense grids): the second block of a
+      // causal pair (same head), else the first block of the next virtual
+      // block.  Its Q rows go straight into qop (dead since this item's last S)
+      // and group 0 loads its K(0) into k0s (no wave reads K after the item's
+      // last barrier); both land while this item's O is written.
+      pre = false;
+      if (!packed) {
+        int nbh = bh, nqblk = -1;
+        if (item + 1 < nitems) {
+          nqblk = j_item;
+        } else if (persist && vb + (int)gridDim.x < total) {
+          const int lg = xcd_remap(vb + (int)gridDim.x, total);
+          nbh = lg / per_head;
+          const int nj = lg - nbh * per_head;
+          nqblk = (CAUSAL || paired) ? nqb - 1 - nj : nj;
+        }
+        if (nqblk >= 0) {
+          const SeqSpan sn = seq_span(sh, nbh / sh.H, nbh % sh.H);
+          const auto rqn = make_rsrc(Q + sn.q_row0 * D, (uint32_t)sn.nq * D * 2);
+          const auto rkn = make_rsrc(K + sn.k_row0 * D, (uint32_t)sn.nk * D * 2);
+          const int qrn = nqblk * C::BM + 128 * grp + 32 * wg + l32;
 #pragma unroll
-        for (int mb = 0; mb < C::MB_O; ++mb)
+          for (int kk = 0; kk < C::KSTEPS; ++kk)
+            qop[kk] = __builtin_bit_cast(op8, buf_load16(rqn, (uint32_t)qrn * C::ROWB + (16 * kk + 8 * h) * 2));
+          if (grp == 0) {
+#pragma unroll
+            for (int q = 0; q < C::LPG; ++q) issue_load(rkn, rkn, q, k0s, nullptr, 0, 0);
+          }
+          pre = true;
+        }
+      }
+      // the 8 O stores below must follow those loads (the next item waits for
+      // the loads with vmcnt 8)
+      __builtin_amdgcn_sched_barrier(0);
+      char* const stg = (w < 4 ? v0s : v1s) + (w & 3) * 4096;
+      // O stores through a buffer resource over this head's rows: rows past Nq
+      // fall outside it and are dropped, so every wave issues exactly 8 stores
+      const auto ro = make_rsrc(O + qbase, (uint32_t)Nq * D * 2);
+      // lane index made opaque here, so that the staging addresses (the same for
+      // every item) are formed in the epilogue instead of being kept in registers
+      // across the tile loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int sr = ln & 31, sh_ = ln >> 5;
+#pragma unroll
+      for (int pass = 0; pass < D / 64; ++pass) {
+#pragma unroll
+        for (int mb2 = 0; mb2 < 2; ++mb2)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
+            const int mb = 2 * pass + mb2, chunk = 4 * mb2 + g;
             const op2 x0 = M::pack2(o[mb][4 * g + 0] * inv, o[mb][4 * g + 1] * inv);
             const op2 x1 = M::pack2(o[mb][4 * g + 2] * inv, o[mb][4 * g + 3] * inv);
             u32x2 u;
             u[0] = __builtin_bit_cast(uint32_t, x0);
             u[1] = __builtin_bit_cast(uint32_t, x1);
-            *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g + 4 * h) = u;
+            lds_store<u32x2>(stg, sr * 128 + 16 * (chunk ^ (sr & 7)) + 8 * sh_, u);
           }
-        if (LSE != nullptr && h == 0) LSE[sp.q_row0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 8 * j + (ln >> 3), c = ln & 7;
+          const u32x4 x = lds_load<u32x4>(stg, r * 128 + 16 * (c ^ (r & 7)));
+          __builtin_amdgcn_raw_buffer_store_b128(x, ro, (uint32_t)(qmin_w + r) * C::ROWB + 128 * pass + 16 * c, 0, 0);
+        }
       }
     }  // work items
   }  // virtual blocks
