@@ -450,6 +450,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         }
         __builtin_amdgcn_s_waitcnt(0);
       } else {
+        // s_waitcnt immediate 0x0078: vmcnt 8 (bits 3:0, 15:14), expcnt 7 = no
+        // wait (bits 6:4), lgkmcnt 0 (bits 11:8)
         __builtin_amdgcn_s_waitcnt(0x0078);
       }
       __syncthreads();
