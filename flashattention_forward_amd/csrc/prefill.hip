@@ -497,12 +497,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       // a row that saw no key (packed batches only) has l = 0: O = 0, LSE = -inf
       const float l_tot = pair_sum(l_run);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      // O leaves through LDS, so that every global store writes whole 128-byte
-      // pieces of rows (the accumulator layout gives a lane 8-byte pieces of one
-      // row, 16 bytes apart).  Each wave stages its 32 rows 64 columns at a time
-      // in a private 4 KB region of the V tile buffers, which no wave reads or
-      // loads into between the item's last barrier and the next item's first;
-      // 16-byte chunks are XOR-swizzled by row.
       static_assert(D % 64 == 0, "O is staged 64 columns at a time");
       if (qrow < Nq && LSE != nullptr && h == 0) LSE[sp.q_row0 + qrow] = (m_run + __log2f(l_tot)) * kLn2;
       // the next item of this workgroup (dense grids): the second block of a
@@ -539,6 +533,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       // the 8 O stores below must follow those loads (the next item waits for
       // the loads with vmcnt 8)
       __builtin_amdgcn_sched_barrier(0);
+      // O leaves through LDS, so that every global store writes whole 128-byte
+      // pieces of rows (the accumulator layout gives a lane 8-byte pieces of one
+      // row, 16 bytes apart).  Each wave stages its 32 rows 64 columns at a time
+      // in a private 4 KB region of the V tile buffers, which no wave reads or
+      // loads into between the item's last barrier and the next item's first;
+      // 16-byte chunks are XOR-swizzled by row.
       char* const stg = (w < 4 ? v0s : v1s) + (w & 3) * 4096;
       // O stores through a buffer resource over this head's rows: rows past Nq
       // fall outside it and are dropped, so every wave issues exactly 8 stores
