@@ -41,3 +41,17 @@ def test_stale_record_is_refused(tmp_path):
     p.write_text(json.dumps(rec))
     assert bench._current_record(str(p)) is None
     assert bench._current_record(str(tmp_path / "missing.json")) is None
+
+
+def test_mfma_record_covers_both_launches():
+    """The non-causal launch's busy cycles per SIMD equal its algorithmic
+    MFMA count (1.0995e12 FLOP / 32,768 FLOP per 32x32x16 MFMA / 1024 SIMDs,
+    32 cycles each); the causal launch needs at least half of that (its
+    visible pairs) and, with whole tiles on the diagonal, a little more."""
+    rec = json.load(open(bench.MFMA_FILE))
+    assert rec["kernel"] == bench.PREFILL_KERNEL
+    assert set(rec["mfma_busy_cycles_per_simd"]) == {1048576}
+    c = rec["causal"]
+    assert c["kernel"] == bench.PREFILL_KERNEL_CAUSAL
+    assert all(524288 <= b <= 1.1 * 524288 for b in c["mfma_busy_cycles_per_simd"])
+    assert len(c["mfma_util_pct"]) == c["dispatches"] == len(c["clock_ghz"])
