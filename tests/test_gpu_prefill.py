@@ -199,6 +199,19 @@ def test_causal_many_heads(F, Nq, Nk, d, dtype):
     assert worst_o <= O_TOL and worst_l <= LSE_TOL
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_persistent_grid_all_heads(F, dtype):
+    """A dense grid with more query blocks than CUs runs on the persistent
+    grid: each workgroup walks several blocks of different heads, requests the
+    next block's Q and first K tile during the current block's epilogue, and
+    writes O through buffer stores whose rows past Nq are dropped.  A ragged
+    Nq (two blocks, the second of 44 rows) and every head compared whole."""
+    w = G.Workload("persistent_heads", 61, 2, 160, 300, 300, 128, dtype, 1.0, False, 128 ** -0.5)
+    q, k, v, O, L = _whole(w, False)
+    out, lse = _run(F, q, k, v, w, False)
+    _check(out, lse, O, L)
+
+
 def test_long_sequence_memory(F):
     """One trading day (N = 23400, 12 heads, fp16): the naive N x N fp16 score
     matrix would take 13.1 GB; the tiled forward allocates nothing beyond its
