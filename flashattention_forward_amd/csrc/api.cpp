@@ -381,7 +381,9 @@ const char* attn_build_info(void) {
          "decode split-KV 256 threads, 8 rows in flight/lane + LSE merge (static 8 MiB scratch variant); "
          "q8 prefill d=128 BM=128 BN=64 (3 workgroups/CU, double-buffered direct-to-LDS K8/V8 tiles), int8 32x32x32 + "
          "fp8 32x32x64 MFMA, V^T via ds_read_b64_tr_b8; "
-         "backward: (lse, D) preprocess, dK/dV kernel (128 keys/WG, 32-query steps, K and V rows resident), "
+         "backward: (lse, D) preprocess, dK/dV kernel (128 keys/WG; d=128 dense non-causal: P/dV and dS/dK wave "
+         "groups ping-ponging MFMA and vector phases over 64-query steps, else 32-query steps with K and V rows "
+         "resident), "
          "dQ kernel (128 queries/WG, 32-key steps), no atomics";
 }
 

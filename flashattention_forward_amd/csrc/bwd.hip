@@ -19,7 +19,10 @@
 //            Per step and wave: S = Q K^T and
 //            dP = dO V^T come out with one key per lane, which is exactly the
 //            A-operand layout of P^T and dS^T, so dV += P^T dO and
-//            dK += dS^T Q follow with dO and Q read transposed from LDS;
+//            dK += dS^T Q follow with dO and Q read transposed from LDS.
+//            At d = 128 on dense non-causal grids bwd_kv_pp takes its place:
+//            the same products split between a P/dV and a dS/dK group of
+//            waves on the forward's ping-pong schedule;
 //   bwd_dq:  a workgroup owns 128 queries (Q and dO in registers) and streams
 //            K and V tiles; S^T = K Q^T and dP^T = V dO^T come out with one
 //            query per lane, the A-operand layout of dS, and dQ += dS K reads
@@ -422,6 +425,324 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bwd_kv, d = 128
+// At d = 128 the dK/dV work of a key block is split between two groups of 4
+// waves that run the forward's ping-pong schedule.  The workgroup owns 128
+// keys; wave w & 3 of either group takes 32 of them.  Group 0 forms P and
+// accumulates dV, group 1 forms dS and accumulates dK, so each wave holds one
+// 128-register accumulator set and one of K, V as its B operand (holding both
+// accumulator sets and K, as the kernel above does, leaves no room for the
+// schedule).  Per query step u (64 queries) a wave has an MFMA phase G_u and
+// a vector phase X_u:
+//   group 0  G_u: dV += P(u-1)^T dO(u-1), then S(u) = Q(u) K^T
+//            X_u: P(u) = exp2(S c - LSE log2 e), masked, packed; P(u) to LDS
+//   group 1  G_u: dK += dS(u-1)^T Q(u-1), then dP(u) = dO(u) V^T
+//            X_u: dS(u) = P(u) (dP(u) - D), with P(u) read back from LDS
+// Group 1 runs its sequence one phase behind group 0, so on every SIMD (one
+// wave of each group) one wave feeds the matrix cores while the other feeds
+// the vector ALU; a workgroup barrier ends every step (every other phase).
+// Step u's Q, dO, (LSE, D) and P tiles are read from phase 2u to phase 2u+3,
+// so three tile sets rotate; group 0 requests step u+1 during its S products
+// in phase 2u, and the barrier that ends phase 2u+1 waits for it.  Dense
+// non-causal grids only (every workgroup walks every query step of its heads).
+template <bool BF16>
+__global__ __launch_bounds__(512, 1) void bwd_kv_pp_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float2* __restrict__ LD, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, SeqShape sh, float c, float scale, int nkb, int total) {
+  constexpr int D = 128;
+  using C = BwdCfg<D>;
+  using M = Mfma<BF16>;
+  typedef typename M::op8 op8;
+  constexpr int SQ = 64;                    // queries per step: two 32-query halves
+  constexpr int TB = SQ * C::ROWB;          // bytes per Q or dO tile
+  constexpr int PWB = 2 * 2 * 64 * 16;      // P of one wave and step: 2 halves x 2 packed operands x 64 lanes x 16 B
+  static_assert(C::BO == 128, "128 keys per workgroup");
+  // three tile sets (step u in set u % 3): Q, dO, (LSE, D) of each half, P
+  __shared__ __attribute__((aligned(1024))) char q0s[TB];
+  __shared__ __attribute__((aligned(1024))) char q1s[TB];
+  __shared__ __attribute__((aligned(1024))) char q2s[TB];
+  __shared__ __attribute__((aligned(1024))) char d0s[TB];
+  __shared__ __attribute__((aligned(1024))) char d1s[TB];
+  __shared__ __attribute__((aligned(1024))) char d2s[TB];
+  __shared__ __attribute__((aligned(256))) char l0s[SQ * 8];
+  __shared__ __attribute__((aligned(256))) char l1s[SQ * 8];
+  __shared__ __attribute__((aligned(256))) char l2s[SQ * 8];
+  __shared__ __attribute__((aligned(1024))) char p0s[4 * PWB];
+  __shared__ __attribute__((aligned(1024))) char p1s[4 * PWB];
+  __shared__ __attribute__((aligned(1024))) char p2s[4 * PWB];
+
+  // work item as in the kernel above: 128 keys of one (batch, K/V head),
+  // each XCD taking a contiguous range of them
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int Hkv = sh.H / sh.group;
+  const int sk = logical / nkb, kb = logical - sk * nkb;
+  const int k0 = kb * C::BO;
+  const int sq = sk / Hkv, hk = sk - sq * Hkv;
+  const SeqSpan sp = seq_span(sh, sq, hk * sh.group);
+  const int Nq = sp.nq, Nk = sp.nk;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, wg = w & 3;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t kbase = sp.k_row0 * D;
+
+  // this wave's keys; group 0 holds their K rows, group 1 their V rows, as B
+  // operands (n = key, k = d)
+  const int kw0 = k0 + 32 * wg;
+  const int key = kw0 + l32;
+  op8 bop[C::KSTEPS];
+  {
+    const auto rb = make_rsrc((grp == 0 ? K : V) + kbase, (uint32_t)Nk * D * 2);
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk)
+      bop[kk] = __builtin_bit_cast(op8, buf_load16(rb, (uint32_t)key * C::ROWB + (16 * kk + 8 * h) * 2));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the query steps of every query head of the group in turn: step u is step
+  // u % nper of head u / nper
+  const int nper = (Nq + SQ - 1) / SQ;
+  const int nu = sh.group * nper;
+
+  // tile loads of step u, issued by the 4 waves of group 0: wave wg fills 1 KB
+  // blocks LPG wg .. LPG wg + LPG-1 of the Q and of the dO tile, and waves 0
+  // and 1 fetch the LSE and D of half 0 and half 1 (lane i < 32: row i's LSE,
+  // lane 32 + i: its D, so a half's 32 LSE values are followed by its 32 D values)
+  constexpr int LPG = TB / 1024 / 4;
+  uint32_t goff[LPG];
+#pragma unroll
+  for (int i = 0; i < LPG; ++i) {
+    const int row = (LPG * wg + i) * C::RPI + lane / C::SPR, ps = lane % C::SPR;
+    goff[i] = (uint32_t)row * C::ROWB + 16 * (ps ^ bswz<D>(row));
+  }
+  typedef __amdgpu_buffer_rsrc_t Rsrc;
+  struct StepSrc {
+    Rsrc rq, rdo, rld;
+    uint32_t row0;  // the step's first query row
+  };
+  auto step_src = [&](int u) __attribute__((always_inline)) {
+    const int gi = u / nper;
+    const size_t qrow0 = sp.q_row0 + (size_t)gi * Nq;
+    StepSrc r;
+    r.rq = make_rsrc(Q + qrow0 * D, (uint32_t)Nq * D * 2);
+    r.rdo = make_rsrc(dO + qrow0 * D, (uint32_t)Nq * D * 2);
+    r.rld = make_rsrc(LD + qrow0, (uint32_t)Nq * 8);
+    r.row0 = (uint32_t)((u - gi * nper) * SQ);
+    return r;
+  };
+  // load i of this wave (i < LPG: a Q block, else a dO block)
+  auto load_one = [&](const StepSrc& r, int i, char* qt, char* dt) __attribute__((always_inline)) {
+    if (i < LPG)
+      bwd_load_lds16(r.rq, qt + 1024 * (LPG * wg + i), r.row0 * C::ROWB + goff[i]);
+    else
+      bwd_load_lds16(r.rdo, dt + 1024 * (LPG * wg + i - LPG), r.row0 * C::ROWB + goff[i - LPG]);
+  };
+  auto load_ld = [&](const StepSrc& r, char* lt) __attribute__((always_inline)) {
+    if (w < 2) bwd_load_lds4(r.rld, lt + 256 * w, (r.row0 + 32 * w + (lane & 31)) * 8 + 4 * (lane >> 5));
+  };
+  // row reads and transposing reads of a 32-row half, as in the kernel above
+  const uint32_t ra_base = l32 * C::ROWB, ra_x = 16 * (h ^ bswz<D>(l32));
+  uint32_t tr_base[2], tr_x[2];
+  {
+    const int r16 = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = (r16 >> 2) + 4 * h + 8 * hi;
+      tr_base[hi] = row * C::ROWB + 8 * (r16 & 1);
+      tr_x[hi] = 16 * ((2 * g1 + ((r16 & 3) >> 1)) ^ bswz<D>(row));
+    }
+  }
+  auto tr_load = [&](const char* t, int nb, int ti) __attribute__((always_inline)) {
+    const s16x4 lo = lds_read_tr16(t, tr_base[0] + ((64u * nb) ^ tr_x[0]) + 16 * ti * C::ROWB);
+    const s16x4 hi = lds_read_tr16(t, tr_base[1] + ((64u * nb) ^ tr_x[1]) + 16 * ti * C::ROWB);
+    return __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // rows of half t times bop over d, operand reads two ahead; with LDS_ (group
+  // 0, when a next step exists) also loads LPG of that step's tile blocks,
+  // lq .. lq + LPG-1, one every other MFMA, so the address unit sees a steady
+  // trickle instead of every wave's loads at once
+  auto row_gemm = [&](const char* t, auto LDS_, const StepSrc& nx, int lq, char* qn, char* dn)
+                      __attribute__((always_inline)) {
+    constexpr bool L = decltype(LDS_)::value;
+    f32x16 acc = f32x16{};
+    op8 ar[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ar[kk] = lds_load<op8>(t, ra_base + ((32u * kk) ^ ra_x));
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      const op8 x = ar[kk & 1];
+      if (kk + 2 < C::KSTEPS) ar[kk & 1] = lds_load<op8>(t, ra_base + ((32u * (kk + 2)) ^ ra_x));
+      acc = M::mma(x, bop[kk], acc);
+      if (L && (kk & 1)) load_one(nx, lq + kk / 2, qn, dn);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (kk + 2 < C::KSTEPS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if (L && (kk & 1)) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    }
+    return acc;
+  };
+  static_assert(2 * (C::KSTEPS / 2) == 2 * LPG, "the S products of a step carry its 2 LPG tile loads");
+  f32x16 acc[C::NBD];  // group 0: dV, group 1: dK (before the scale)
+#pragma unroll
+  for (int nb = 0; nb < C::NBD; ++nb) acc[nb] = f32x16{};
+  // acc[nb] += am[ti] * (half t read transposed), B operands two ahead
+  auto tr_gemm = [&](const char* t, const op8* am) __attribute__((always_inline)) {
+    constexpr int NT = 2 * C::NBD;
+    op8 br[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) br[u] = tr_load(t, u % C::NBD, u / C::NBD);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const op8 x = br[u & 1];
+      if (u + 2 < NT) br[u & 1] = tr_load(t, (u + 2) % C::NBD, (u + 2) / C::NBD);
+      acc[u % C::NBD] = M::mma(am[u / C::NBD], x, acc[u % C::NBD]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (u + 2 < NT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+  };
+
+  // S(u) or dP(u) between the MFMA and vector phases, and P(u) or dS(u),
+  // packed, between the vector phase and the next MFMA phase; element i of
+  // half j: query 32 j + 8 (i/4) + 4h + i%4 of the step, key of this lane
+  f32x16 sx[2];
+  op8 px[2][2];
+  // G_u of this wave's group: (qc, dc) hold step u, (qp, dp) step u-1; group
+  // 0 also loads step u+1 into (qn, dn, ln)
+  auto gphase = [&](int u, const char* qc, const char* dc, const char* qp, const char* dp, char* qn, char* dn,
+                    char* ln) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    if (u >= 1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (grp == 0)
+          tr_gemm(dp + 32 * j * C::ROWB, px[j]);  // dV += P^T dO
+        else
+          tr_gemm(qp + 32 * j * C::ROWB, px[j]);  // dK += dS^T Q
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (u < nu) {
+      if (grp == 0 && u + 1 < nu) {
+        const StepSrc nx = step_src(u + 1);
+        load_ld(nx, ln);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          sx[j] = row_gemm(qc + 32 * j * C::ROWB, std::true_type{}, nx, LPG * j, qn, dn);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        const StepSrc none{};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          sx[j] = row_gemm((grp == 0 ? qc : dc) + 32 * j * C::ROWB, std::false_type{}, none, 0, nullptr, nullptr);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // X_u: lt holds step u's (LSE, D), pt its P
+  auto xphase = [&](int u, const char* lt, char* pt) __attribute__((always_inline)) {
+    if (u < 0 || u >= nu) return;
+    const int q0 = (u % nper) * SQ;
+    char* const pw = pt + wg * PWB;  // this key block's P, written by group 0, read by group 1
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int qj = q0 + 32 * j;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 Lr = lds_load<f32x4>(lt, 256 * j + (8 * a + 4 * h) * 4);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) sx[j][4 * a + b] = __builtin_amdgcn_exp2f(fmaf(sx[j][4 * a + b], c, -Lr[b]));
+        }
+        // queries past Nq are masked, on the last half only
+        if (qj + 32 > Nq) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = qj + 8 * (i >> 2) + 4 * h + (i & 3);
+            const uint32_t hide = qi >= Nq ? 0xFFFFFFFFu : 0u;
+            const float v = sx[j][i];  // copied out first (a bit cast of a vector element in place misreads)
+            sx[j][i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & ~hide);
+          }
+        }
+        px[j][0] = pack8<M>(sx[j], 0);
+        px[j][1] = pack8<M>(sx[j], 8);
+        lds_store<u32x4>(pw, (2 * j) * 1024 + 16 * lane, __builtin_bit_cast(u32x4, px[j][0]));
+        lds_store<u32x4>(pw, (2 * j + 1) * 1024 + 16 * lane, __builtin_bit_cast(u32x4, px[j][1]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const op8 pa[2] = {__builtin_bit_cast(op8, lds_load<u32x4>(pw, (2 * j) * 1024 + 16 * lane)),
+                           __builtin_bit_cast(op8, lds_load<u32x4>(pw, (2 * j + 1) * 1024 + 16 * lane))};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 Dr = lds_load<f32x4>(lt, 256 * j + 128 + (8 * a + 4 * h) * 4);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int i = 4 * a + b;
+            sx[j][i] = op8_elem<M>(pa[i >> 3], i & 7) * (sx[j][i] - Dr[b]);
+          }
+        }
+        px[j][0] = pack8<M>(sx[j], 0);
+        px[j][1] = pack8<M>(sx[j], 8);
+      }
+    }
+  };
+  // phases 2u (group 0: G_u, group 1: X_{u-1}) and 2u+1 (group 0: X_u,
+  // group 1: G_u); set c holds step u, set p step u-1, and step u+1 is
+  // loaded into set n
+  auto pair = [&](int u, const char* qc, const char* dc, const char* lc, char* pc, const char* qp, const char* dp,
+                  const char* lp, char* pp, char* qn, char* dn, char* ln) __attribute__((always_inline)) {
+    if (grp == 0)
+      gphase(u, qc, dc, qp, dp, qn, dn, ln);
+    else
+      xphase(u - 1, lp, pp);
+    if (grp == 0)
+      xphase(u, lc, pc);
+    else
+      gphase(u, qc, dc, qp, dp, qn, dn, ln);
+    // the loads of step u+1 have landed, P(u) is written, and every wave is
+    // done with step u-1's set, which step u+2 overwrites next
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  if (nu > 0 && grp == 0) {
+    const StepSrc s0src = step_src(0);
+    load_ld(s0src, l0s);
+#pragma unroll
+    for (int i = 0; i < 2 * LPG; ++i) load_one(s0src, i, q0s, d0s);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int u = 0; u <= nu; u += 3) {
+    pair(u, q0s, d0s, l0s, p0s, q2s, d2s, l2s, p2s, q1s, d1s, l1s);
+    if (u + 1 <= nu) pair(u + 1, q1s, d1s, l1s, p1s, q0s, d0s, l0s, p0s, q2s, d2s, l2s);
+    if (u + 2 <= nu) pair(u + 2, q2s, d2s, l2s, p2s, q1s, d1s, l1s, p1s, q0s, d0s, l0s);
+  }
+
+  // element i of block nb: key kw0 + 8 (i/4) + 4h + i%4, column 32 nb + l32
+  uint16_t* const out = grp == 0 ? dV : dK;
+  const float osc = grp == 0 ? 1.f : scale;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kr = kw0 + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (kr < Nk) {
+      uint16_t* po = out + kbase + (size_t)kr * D + l32;
+#pragma unroll
+      for (int nb = 0; nb < C::NBD; ++nb) po[32 * nb] = to_half_bits<BF16>(acc[nb][i] * osc);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- bwd_dq
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
@@ -601,11 +922,25 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   const int nkb = (max_nk + C::BO - 1) / C::BO;
   const int totk = nkb * nseq * (sh.H / sh.group);
   if (totk > 0) {
-    hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, CAUSAL>), dim3(totk), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
-                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk,
-                       sh.cu_q != nullptr ? totk / nkb : max(1, totk / nkb / 8));
+    const int chunk = sh.cu_q != nullptr ? totk / nkb : max(1, totk / nkb / 8);
+    // the split kernel at d = 128 on dense non-causal grids, where every
+    // workgroup walks all query steps; causal and packed grids have short key
+    // blocks whose fixed costs the two workgroups per CU of the other kernel
+    // overlap better than the split kernel's one
+    bool split = false;
+    if constexpr (D == 128 && !CAUSAL) split = sh.cu_q == nullptr;
+    if (split) {
+      if constexpr (D == 128 && !CAUSAL)
+        hipLaunchKernelGGL((bwd_kv_pp_kernel<BF16>), dim3(totk), dim3(512), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
+                           static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk);
+    } else {
+      hipLaunchKernelGGL((bwd_kv_kernel<D, BF16, CAUSAL>), dim3(totk), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), ld,
+                         static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), sh, c, scale, nkb, totk, chunk);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
