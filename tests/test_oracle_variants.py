@@ -164,3 +164,52 @@ def test_int8_per_tensor_mistake_is_caught():
         return np.clip(np.floor(x / s), -127, 127).astype(np.int8), s
     with pytest.raises(AssertionError):
         P.pin_int8_per_tensor(floor_q)
+
+
+def test_prob_int8_rounding_pin():
+    """P8 = rint(127 P): brute force against Python's round (half to even) on
+    probabilities whose 127 P are exact halves and on random ones; the range
+    is 0 .. 127 with P = 1 at 127."""
+    halves = np.arange(0, 255) / 2.0          # 127 P = 0, 0.5, ..., 127
+    p = halves / 127.0
+    exact = 127.0 * p == halves               # keep the ties that survive the division
+    got = Q.quantize_prob_int8(p)
+    want = np.array([round(float(x)) for x in 127.0 * p])
+    assert np.array_equal(got, want)
+    assert exact.sum() > 100 and np.array_equal(got[exact], [round(x) for x in halves[exact]])
+    assert got[exact][1] == 0 and got[exact][3] == 2   # 0.5 -> 0, 1.5 -> 2
+    r = np.random.default_rng(3).random(1000)
+    assert np.array_equal(Q.quantize_prob_int8(r), [round(127.0 * x) for x in r])
+    assert Q.quantize_prob_int8(np.array([0.0, 1.0])).tolist() == [0.0, 127.0]
+
+
+def test_i8_whole_tensor_pin():
+    """The all-INT8 forward on [B, H, N, d] tensors, from unquantised inputs:
+    (a) Q = 0 gives uniform P (P8 = 127 on every key), so each head's O is
+    s_v times the mean of its own V8 rows and LSE = ln Nk; V differs per
+    head, so a head taking another head's K/V fails; (b) orthogonal keys and
+    a query aligned with one key at a large score select that key's V8 row;
+    V8 and s_v are the per-tensor int8 codes of V (within s_v / 2 of V)."""
+    rng = np.random.default_rng(21)
+    B, H, Nq, Nk, d = 2, 3, 4, 6, 8
+    v = rng.standard_normal((B, H, Nk, d)).astype(np.float32) + np.arange(B * H).reshape(B, H, 1, 1)
+    k = rng.standard_normal((B, H, Nk, d)).astype(np.float32)
+    O, L, qi = Q.attention_i8(np.zeros((B, H, Nq, d), np.float32), k, v, 0.5)
+    assert O.shape == (B, H, Nq, d) and L.shape == (B, H, Nq)
+    sv = float(qi["sv"])
+    assert abs(sv - float(np.max(np.abs(v))) / 127.0) <= 1e-6 * sv
+    assert np.max(np.abs(qi["v8"] * sv - v)) <= 0.5 * sv * (1 + 1e-6)
+    for b in range(B):
+        for h in range(H):
+            want = sv * qi["v8"][b, h].astype(np.float64).mean(axis=0)
+            assert np.max(np.abs(O[b, h] - want)) <= 1e-12
+    assert np.max(np.abs(L - np.log(Nk))) <= 1e-12
+    # (b): key j = e_j * 4, query i aligned with key i; scores 4 * 4 * scale apart
+    k = np.zeros((1, 1, Nk, d), np.float32)
+    k[0, 0, np.arange(Nk), np.arange(Nk)] = 4.0
+    q = np.zeros((1, 1, Nq, d), np.float32)
+    q[0, 0, np.arange(Nq), np.arange(Nq)] = 4.0
+    v1 = v[:1, :1]
+    O, _, qi = Q.attention_i8(q, k, v1, 4.0)   # exp(-64) below 127's rounding: P8 one-hot
+    for i in range(Nq):
+        assert np.max(np.abs(O[0, 0, i] - float(qi["sv"]) * qi["v8"][0, 0, i])) <= 1e-12
