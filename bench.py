@@ -60,6 +60,7 @@ METRIC = "attn fwd TFLOP/s & % MFMA peak (prefill); HBM GB/s & % peak (decode)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # dense fp8 / int8
 PEAK_HBM_GBS = 8000.0         # HBM3E
+PEAK_CLOCK_GHZ = 2.4          # the engine clock the MFMA peaks are quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4k_traffic.json")
 COPY_BYTES = 1 << 30          # bytes read (and written) by one calibration copy
 PREFILL_KERNEL = "prefill_kernel<128, true, false, 0>"   # bf16, non-causal, all exp2 on v_exp_f32
@@ -71,6 +72,12 @@ KERNEL_SOURCES = ["flashattention_forward_amd/csrc/prefill.hip", "flashattention
                   "flashattention_forward_amd/csrc/seq_shape.h"]
 DECODE_SOURCES = ["flashattention_forward_amd/csrc/decode.hip", "flashattention_forward_amd/csrc/common.h",
                   "flashattention_forward_amd/csrc/seq_shape.h"]
+
+
+def _median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
 def kernel_source_sha(sources=None) -> str:
@@ -538,6 +545,11 @@ def main():
                      "mfma_util_counted": None if mf is None else {
                          "pct": mf["mfma_util_pct"], "clock_ghz": mf["clock_ghz"],
                          "causal_pct": mf.get("causal", {}).get("mfma_util_pct"),
+                         # the nameplate peak scaled to the median clock of the counter run, and this
+                         # run's throughput against it (the clock was counted in another run)
+                         "peak_at_counted_clock": round(PEAK_BF16_TFLOPS * _median(mf["clock_ghz"]) / PEAK_CLOCK_GHZ, 1),
+                         "frac_at_counted_clock": round(achieved / (PEAK_BF16_TFLOPS * _median(mf["clock_ghz"])
+                                                                    / PEAK_CLOCK_GHZ), 4),
                          "source": "profiles/prefill_4k_mfma.json (rocprofv3 MfmaUtil)"}},
         "kernels": {
             "prefill_noncausal": {"ms": round(per[0] * 1e3, 4), "tflops": round(flops_nc / per[0] / 1e12, 3),
