@@ -285,3 +285,90 @@ def test_decode_full_size_sampled(F):
         f = lambda x: G.to_f64(x[b, h], "bf16")
         O, L = A.attention_head(f(q), f(k), f(v), w.scale)
         assert np.abs(o_all[b, h] - O).max() <= O_TOL and np.abs(l_all[b, h] - L).max() <= LSE_TOL
+
+
+def test_max_span_head(F):
+    """One K/V head at the largest span the library accepts: 2^31 - 2^16
+    bytes, 8,388,352 keys of d = 128 bf16, the limit of the 32-bit buffer
+    offsets (the prefill also requests the tile one past the last, which must
+    read as zero and not wrap).  A 256-query block against it, non-causal and
+    causal (bottom-right aligned: row r sees keys 0 .. r + Nk - 256), and the
+    split-KV decode of the block's last query.  Inputs: K and V are the 64
+    seeded heads of a [1, 64, 131068, 128] draw laid end to end as one head
+    (64 generator streams, so the draw runs in parallel), Q one seeded head.
+    The oracle evaluates sampled rows over 2^21-key chunks and merges the
+    chunks' (O, LSE) states; for the causal rows the last chunk is cut at the
+    row's last visible key."""
+    import torch
+    from tests.gpu_util import from_dev, nan_like, to_dev
+    d, nk_part, parts, Nq = 128, 131068, 64, 256
+    Nk = nk_part * parts
+    assert Nk * d * 2 == (1 << 31) - (1 << 16)
+    wkv = G.Workload("max_span_kv", 62, 1, parts, Nq, nk_part, d, "bf16", 1.0, False, d ** -0.5)
+    wq = G.Workload("max_span_q", 63, 1, 1, Nq, Nq, d, "bf16", 1.0, False, d ** -0.5)
+    print(f"  drawing K, V: {Nk} keys x {d} (bf16)", flush=True)
+    k = G.draw_tensor(wkv, "k", threads=16).reshape(1, 1, Nk, d)
+    v = G.draw_tensor(wkv, "v", threads=16).reshape(1, 1, Nk, d)
+    q = G.draw_tensor(wq, "q", threads=1)
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    res = {}
+    for causal in (False, True):
+        out = nan_like(tq)
+        lse = torch.full((1, 1, Nq), float("nan"), device="cuda")
+        print(f"  gpu: max-span prefill Nq={Nq} Nk={Nk} d={d} bf16 causal={causal}", flush=True)
+        F.attn_fwd(tq, tk, tv, causal=causal, scale=wq.scale, out=out, lse=lse)
+        torch.cuda.synchronize()
+        res[causal] = (from_dev(out)[0, 0], from_dev(lse)[0, 0])
+    out_d = nan_like(tq[:, :, Nq - 1:])
+    lse_d = torch.full((1, 1, 1), float("nan"), device="cuda")
+    print(f"  gpu: max-span decode Nk={Nk}", flush=True)
+    F.attn_fwd(tq[:, :, Nq - 1:].contiguous(), tk, tv, scale=wq.scale, out=out_d, lse=lse_d)
+    torch.cuda.synchronize()
+    dec = (from_dev(out_d)[0, 0, 0], from_dev(lse_d)[0, 0, 0])
+    del tk, tv
+    torch.cuda.empty_cache()
+
+    rows = [0, 1, 31, 32, 128, 200, 254, 255]
+    off = Nk - Nq
+    q64 = G.to_f64(q[0, 0], "bf16")
+    chunk = 1 << 21
+    parts_nc, parts_c = [], []
+    for a in range(0, Nk, chunk):
+        b = min(Nk, a + chunk)
+        print(f"  oracle: keys {a} .. {b - 1}", flush=True)
+        k64 = G.to_f64(k[0, 0, a:b], "bf16")
+        v64 = G.to_f64(v[0, 0, a:b], "bf16")
+        parts_nc.append(A.attention_rows(q64, k64, v64, rows, wq.scale, False))
+        oc, lc = [], []
+        for r in rows:
+            n = min(b, r + off + 1) - a          # this chunk's keys visible to row r
+            if n == b - a:
+                o1, l1 = A.attention_rows(q64, k64, v64, [r], wq.scale, False)
+            else:
+                o1, l1 = A.attention_rows(q64, k64[:n], v64[:n], [r], wq.scale, False)
+            oc.append(o1[0])
+            lc.append(l1[0])
+        parts_c.append((np.array(oc), np.array(lc)))
+    want = {}
+    for causal, ps in ((False, parts_nc), (True, parts_c)):
+        want[causal] = R.merge_states(np.stack([p[0] for p in ps]), np.stack([p[1] for p in ps]))
+    # averaged over 8.4 M keys the outputs are small (|O| ~ 1e-3), so O is also
+    # held to the bf16 output rounding: half an ulp of bf16 (8 significant
+    # bits) is at most 2^-8 of the value, and the fp32 sums add about 1e-5 of
+    # it; 2^-7 of its row's largest element leaves a factor of two
+    worst_o = worst_l = worst_rel = 0.0
+    for causal in (False, True):
+        o, l = res[causal]
+        assert np.isfinite(o).all() and np.isfinite(l).all()
+        err = np.abs(o[rows] - want[causal][0])
+        worst_o = max(worst_o, err.max())
+        worst_rel = max(worst_rel, (err.max(axis=1) / np.abs(want[causal][0]).max(axis=1)).max())
+        worst_l = max(worst_l, np.abs(l[rows] - want[causal][1]).max())
+    # the decode query is row 255, which sees every key under both masks
+    err = np.abs(dec[0] - want[False][0][-1])
+    worst_o = max(worst_o, err.max())
+    worst_rel = max(worst_rel, err.max() / np.abs(want[False][0][-1]).max())
+    worst_l = max(worst_l, abs(dec[1] - want[False][1][-1]))
+    print(f"  max-span sampled max|dO|={worst_o:.3e} (max per-row rel {worst_rel:.3e}) max|dLSE|={worst_l:.3e}",
+          flush=True)
+    assert worst_o <= O_TOL and worst_l <= LSE_TOL and worst_rel <= 2.0 ** -7
