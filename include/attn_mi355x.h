@@ -88,8 +88,10 @@ size_t attn_fwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
  *   after the call are unspecified.
  * Nq == 1 dispatches to the split-KV decode kernels (partials over key
  * ranges, then a log-sum-exp merge); every other Nq runs the tiled prefill
- * kernel, which addresses one head of Q, K or V in 32 bits: Nq*d*2 and
- * Nk*d*2 must stay below 2^32 bytes (ATTN_E_INVALID otherwise).
+ * kernel, which addresses one head of Q, K or V through 32-bit buffer
+ * offsets: Nq*d*2 and Nk*d*2 must be at most 2^31 - 2^16 bytes (the headroom
+ * keeps the offset of the tile requested past Nk below 2^31), else
+ * ATTN_E_INVALID.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
@@ -194,7 +196,8 @@ int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* ou
  *   (B*H*Nq float pairs: lse in base 2 and D), 16-byte aligned; its contents
  *   after the call are unspecified.
  *   d in {64, 128}; B, H, Nq, Nk >= 1; causal needs Nq <= Nk; one head of
- *   q, k, v stays below 2^32 bytes (ATTN_E_INVALID otherwise).
+ *   q, k, v spans at most 2^31 - 2^16 bytes, as for attn_fwd (ATTN_E_INVALID
+ *   otherwise).
  * Three kernels run on `stream`: the (lse, D) preprocess, a key-block kernel
  * for dK and dV and a query-block kernel for dQ.  No atomics: the result does
  * not depend on scheduling.
